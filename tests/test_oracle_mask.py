@@ -1,0 +1,187 @@
+"""Pins for oracle.block_mask: closed forms, numpy's quantile, pure-Python enumeration and invariants."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as A
+from oracle import block_mask as M
+
+
+def rnd(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ------------------------------------------------------------------------------------------------ stats (step 1-2)
+def test_single_key_block_closed_form():
+    """All keys of a block zero except one key x: centroid x/b, radius (b-1)/b * |x| (the other keys sit at
+    |x|/b, closer), and a query block of identical rows has that row as its mean."""
+    b, D = 8, 5
+    x = np.array([3.0, -4.0, 0.0, 12.0, 0.0])          # |x| = 13
+    k = np.zeros((1, 1, 2 * b, D))
+    k[0, 0, 3] = x
+    k[0, 0, b:] = 1.0                                    # second block: identical keys -> radius 0
+    q = np.zeros((1, 2, 2 * b, D))
+    q[0, 1, :b] = x
+    qbar, kbar, r = M.block_stats(q, k, b)
+    np.testing.assert_allclose(kbar[0, 0, 0], x / b, atol=1e-15)
+    assert abs(r[0, 0, 0] - (b - 1) / b * 13.0) < 1e-13
+    assert r[0, 0, 1] == 0.0
+    np.testing.assert_allclose(kbar[0, 0, 1], 1.0)
+    np.testing.assert_allclose(qbar[0, 1, 0], x, atol=1e-15)
+    np.testing.assert_allclose(qbar[0, 0], 0.0)
+
+
+def test_stats_equal_explicit_loops():
+    b = 4
+    q, k = rnd(1, 1, 4, 12, 3), rnd(2, 1, 2, 12, 3)
+    qbar, kbar, r = M.block_stats(q, k, b)
+    for h in range(4):
+        for i in range(3):
+            for d in range(3):
+                assert abs(qbar[0, h, i, d] - sum(q[0, h, i * b + t, d] for t in range(b)) / b) < 1e-14
+    for g in range(2):
+        for j in range(3):
+            c = [sum(k[0, g, j * b + t, d] for t in range(b)) / b for d in range(3)]
+            far = max(math.sqrt(sum((k[0, g, j * b + t, d] - c[d]) ** 2 for d in range(3))) for t in range(b))
+            assert abs(r[0, g, j] - far) < 1e-13
+
+
+# ---------------------------------------------------------------------------------------------- quantiles (step 3)
+@pytest.mark.parametrize("n", [1, 2, 3, 10, 11, 512, 1024, 1000])
+@pytest.mark.parametrize("pct", [0, 10, 50, 90, 100, 37])
+def test_quantile_matches_numpy_linear(n, pct):
+    x = np.sort(np.random.default_rng(n * 101 + pct).random(n) * 10)
+    mine = M.quantile_type7(x, pct)
+    ref = float(np.quantile(x, pct / 100.0, method="linear"))
+    assert abs(mine - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+@pytest.mark.parametrize("n,expected", [(512, 52), (1024, 103), (100, 10)])
+def test_flag_count_with_alpha_one(n, expected):
+    """With alpha = 1 the threshold is the interpolated 90th percentile, which sits strictly between the two
+    order statistics around (n-1)*0.9 when that position is not an integer; the count above it is
+    n-1-floor(0.9(n-1))."""
+    x = np.random.default_rng(n).permutation(np.arange(n, dtype=np.float64) * 0.37 + 1.0)
+    med, p90, tau = M.rescue_threshold(x, 1.0)
+    assert int((x > tau).sum()) == n - 1 - (9 * (n - 1)) // 10 == expected
+    assert abs(med - float(np.median(x))) < 1e-12
+
+
+def test_threshold_moves_with_alpha_in_the_right_direction():
+    x = np.random.default_rng(3).random(200)
+    _, _, t0 = M.rescue_threshold(x, 0.0)
+    _, _, t1 = M.rescue_threshold(x, 1.0)
+    _, _, t2 = M.rescue_threshold(x, 2.0)
+    assert abs(t0 - np.median(x)) < 1e-15 and t0 < t1 < t2
+    assert abs(t2 - (2 * np.quantile(x, 0.9) - np.median(x))) < 1e-12
+    assert M.rescue_threshold(x, math.inf)[2] == math.inf
+
+
+# -------------------------------------------------------------------------------------------- select (steps 4-7)
+def brute_mask(qbar, kbar, rad, scale, keep, alpha, G, lo=50, hi=90):
+    """Pure-Python statement of the rule for tiny sizes (sorted() with an explicit key, Fraction ceilings)."""
+    B, Hq, nb, D = qbar.shape
+    out = np.zeros((B, Hq, nb, nb), dtype=np.uint8)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            xs = sorted(float(r) for r in rad[b, g])
+            def qt(p):
+                pos = Fraction((len(xs) - 1) * p, 100)
+                lo_i = math.floor(pos)
+                f = float(pos - lo_i)
+                return xs[lo_i] if lo_i + 1 >= len(xs) or f == 0 else xs[lo_i] + f * (xs[lo_i + 1] - xs[lo_i])
+            tau = math.inf if math.isinf(alpha) else qt(lo) + alpha * (qt(hi) - qt(lo))
+            for i in range(nb):
+                score = {j: scale * sum(qbar[b, h, i, d] * kbar[b, g, j, d] for d in range(D)) for j in range(i + 1)}
+                budget = math.ceil(Fraction((i + 1) * keep, 1000))
+                ranked = sorted(range(i + 1), key=lambda j: (-score[j], j))
+                for j in range(i + 1):
+                    if j in ranked[:budget] or rad[b, g, j] > tau or j == i:
+                        out[b, h, i, j] = 1
+    return out
+
+
+@pytest.mark.parametrize("keep,alpha", [(100, 1.0), (300, 0.5), (0, math.inf), (1000, math.inf), (250, math.inf),
+                                        (0, 0.0)])
+def test_mask_equals_enumeration(keep, alpha):
+    b, nb = 4, 8
+    q, k = rnd(40, 1, 4, b * nb, 3), rnd(41, 1, 2, b * nb, 3)
+    res = M.build_mask(q, k, 0.7, b, keep, alpha)
+    qbar, kbar, rad = M.block_stats(q, k, b)
+    np.testing.assert_array_equal(res.mask, brute_mask(qbar, kbar, rad, 0.7, keep, alpha, 2))
+
+
+def test_ties_go_to_the_smaller_block_index():
+    """Integer centroids make exact score ties; the budget must take the earlier blocks."""
+    b, nb, D = 2, 6, 2
+    q = np.zeros((1, 1, b * nb, D)); q[..., 0] = 1.0
+    k = np.zeros((1, 1, b * nb, D))
+    k[0, 0, :, 0] = np.repeat([1.0, 3.0, 3.0, 1.0, 3.0, 0.0], b)       # blocks 1, 2, 4 tie at the top
+    res = M.build_mask(q, k, 1.0, b, keep_permille=400, alpha=math.inf)   # row 5: ceil(6*0.4) = 3 picks
+    assert res.centroid[0, 0, 5].nonzero()[0].tolist() == [1, 2, 4]
+    res2 = M.build_mask(q, k, 1.0, b, keep_permille=200, alpha=math.inf)  # row 5: 2 picks -> the first two ties
+    assert res2.centroid[0, 0, 5].nonzero()[0].tolist() == [1, 2]
+    assert res2.mask[0, 0, 5].nonzero()[0].tolist() == [1, 2, 5]
+
+
+def test_mask_invariants():
+    b, nb = 8, 16
+    q, k = rnd(50, 2, 4, b * nb, 6), rnd(51, 2, 2, b * nb, 6)
+    res = M.build_mask(q, k, 0.5, b, keep_permille=200, alpha=1.0)
+    m = res.mask.astype(bool)
+    assert not np.triu(m, 1).any()
+    assert all(m[..., i, i].all() for i in range(nb))
+    for i in range(nb):
+        assert (res.centroid[..., i, :].sum(-1) == M.centroid_budget(i, 200)).all()
+    np.testing.assert_array_equal(res.kv_count, m.sum(-1))
+    for bb in range(2):
+        for h in range(4):
+            for i in range(nb):
+                c = res.kv_count[bb, h, i]
+                idx = res.kv_index[bb, h, i]
+                assert (np.diff(idx[:c]) > 0).all() and idx[c - 1] == i and (idx[c:] == -1).all()
+                np.testing.assert_array_equal(idx[:c], np.nonzero(m[bb, h, i])[0])
+    full = M.build_mask(q, k, 0.5, b, 1000, 1.0).mask
+    np.testing.assert_array_equal(full, np.broadcast_to(np.tril(np.ones((nb, nb), np.uint8)), full.shape))
+    cen_only = M.build_mask(q, k, 0.5, b, 200, math.inf)
+    eye = np.eye(nb, dtype=bool)
+    np.testing.assert_array_equal(cen_only.mask.astype(bool), cen_only.centroid | eye)
+    diag = M.build_mask(q, k, 0.5, b, 0, math.inf).mask
+    np.testing.assert_array_equal(diag.astype(bool), np.broadcast_to(eye, diag.shape))
+    # rescue flags are shared across the query heads of a kv-head group
+    G = 2
+    for h in range(4):
+        resc = res.rescue[:, h // G]
+        lower = np.tril(np.ones((nb, nb), bool))
+        assert ((m[:, h] | ~(resc[:, None, :] & lower)).all())
+
+
+def test_rescue_catches_every_planted_block():
+    """The planted 6x query keys widen their block's radius far beyond the 90th percentile, so the rescue branch
+    flags every planted block, which the centroid branch alone often misses (mean dilution)."""
+    inp = W.planted_inputs(3, 1, 8, 2, 64 * 64, 64, block=64, planted_per_mille=100)
+    q, k, _ = inp.as_f64()
+    res = M.build_mask(q, k, inp.scale, 64, keep_permille=100, alpha=1.0)
+    for (b, g, j, u, h, t) in inp.planted:
+        assert res.rescue[b, g, j]
+        assert res.mask[b, h, t // 64, j] == 1
+    # and the planted keys do draw the attention of their query row
+    O, _ = A.causal_attention(q[:, :1], k[:, :1], inp.as_f64()[2][:, :1], inp.scale, rows=np.array([0]))
+    assert np.isfinite(O).all()
+
+
+def test_rescue_comparison_is_strict():
+    """alpha = 0 with an odd block count puts tau exactly on the median radius; that block is not flagged."""
+    b, nb, D = 4, 5, 3
+    k = np.zeros((1, 1, b * nb, D))
+    for j, mag in enumerate([4.0, 8.0, 2.0, 16.0, 1.0]):       # radii (b-1)/b * mag, median from mag 4
+        k[0, 0, j * b, 0] = mag
+    q = np.zeros((1, 1, b * nb, D))
+    res = M.build_mask(q, k, 1.0, b, keep_permille=0, alpha=0.0)
+    assert res.tau[0, 0] == res.radius[0, 0, 0]
+    assert res.rescue[0, 0].tolist() == [False, True, False, True, False]
+    assert res.mask[0, 0, 4].nonzero()[0].tolist() == [1, 3, 4]

@@ -1,0 +1,269 @@
+"""Seeded synthetic inputs for the long-context causal attention workloads.
+
+This module is shared by the CPU oracle tests and by the HIP-path tests and benchmark. It holds none of the
+attention arithmetic: only random draws (numpy PCG64, one spawned stream per purpose), round-to-nearest-even
+conversion of the drawn fp32 values to bf16 bit patterns, and index bookkeeping (planted outlier positions,
+the paged KV layout and block table, sampled query rows).
+
+Workload shapes follow the pages:
+  * 32 query heads sharing 4 key/value heads with head_dim 128 and a 128K context, the model shape in
+    "Your 128K Context Is 6x Slower Than It Needs to Be" (section "The rescue branch: two selection paths,
+    one mask"), and the 32K / 128K pair that page measures (sections "The rescue branch" and "What to do
+    today").
+  * A paged KV cache of fixed-size pages that need not be contiguous, walked through a block table
+    ("attention-kernel-optimization", section "PagedAttention (the vLLM revolution)"), for q_len = 1 decode
+    (same page, section "Inference-specific: Flash-Decoding and FlashInfer").
+The pages measure on real prompts and checkpoints that are not available here; these generators stand in for
+them with i.i.d. N(0,1) activations of the same shapes, plus one planted high-attention key per chosen block to
+reproduce the mean-dilution geometry described in "Your 128K Context Is 6x Slower Than It Needs to Be",
+section "Why block-sparse attention underperforms: the mean-dilution trap".
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+BF16_NAN_BITS = np.uint16(0x7FC0)
+
+
+# --------------------------------------------------------------------------------------------------------------
+# bit-level helpers (input preparation only)
+# --------------------------------------------------------------------------------------------------------------
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 with round-to-nearest-even; returns the uint16 bit patterns.
+
+    Inputs are assumed finite (the generators only produce finite values)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def f32_from_bf16_bits(u: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32."""
+    return (np.ascontiguousarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f64_from_bf16_bits(u: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp64."""
+    return f32_from_bf16_bits(u).astype(np.float64)
+
+
+def streams(seed: int, names: List[str]) -> Dict[str, np.random.Generator]:
+    """Independent PCG64 generators, one per purpose, spawned from one SeedSequence."""
+    children = np.random.SeedSequence(seed).spawn(len(names))
+    return {n: np.random.Generator(np.random.PCG64(c)) for n, c in zip(names, children)}
+
+
+def _normal_bf16(rng: np.random.Generator, shape: Tuple[int, ...], chunk_elems: int = 1 << 26) -> np.ndarray:
+    """i.i.d. N(0,1) fp32 draws rounded to bf16 bits, generated in chunks to bound host memory."""
+    total = int(np.prod(shape))
+    out = np.empty(total, dtype=np.uint16)
+    for s in range(0, total, chunk_elems):
+        e = min(total, s + chunk_elems)
+        out[s:e] = bf16_bits_from_f32(rng.standard_normal(e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+# --------------------------------------------------------------------------------------------------------------
+# prefill inputs
+# --------------------------------------------------------------------------------------------------------------
+@dataclass
+class PrefillInputs:
+    """Q [B,Hq,N,D], K/V [B,Hkv,N,D]; bf16 bit patterns (uint16) or fp32 values, D contiguous."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    dtype: str                      # "bf16" | "fp32"
+    scale: float
+    block: Optional[int] = None     # q-block == k-block size for the block-sparse path
+    # planted outliers: tuples (b, kv_head, key_block, slot, q_head, q_row)
+    planted: List[Tuple[int, int, int, int, int, int]] = field(default_factory=list)
+
+    @property
+    def shape(self) -> Tuple[int, int, int, int, int]:
+        B, Hq, N, D = self.q.shape
+        return B, Hq, self.k.shape[1], N, D
+
+    def as_f64(self) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """Exact widening of the very values the GPU receives."""
+        if self.dtype == "bf16":
+            return f64_from_bf16_bits(self.q), f64_from_bf16_bits(self.k), f64_from_bf16_bits(self.v)
+        return self.q.astype(np.float64), self.k.astype(np.float64), self.v.astype(np.float64)
+
+
+def dense_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, D: int, dtype: str = "bf16",
+                 scale: Optional[float] = None) -> PrefillInputs:
+    """i.i.d. N(0,1) Q/K/V. bf16 inputs are fp32 draws rounded to nearest even."""
+    r = streams(seed, ["q", "k", "v", "planted", "rows"])
+    sc = float(1.0 / np.sqrt(D)) if scale is None else float(scale)
+    if dtype == "fp32":
+        q = r["q"].standard_normal((B, Hq, N, D), dtype=np.float32)
+        k = r["k"].standard_normal((B, Hkv, N, D), dtype=np.float32)
+        v = r["v"].standard_normal((B, Hkv, N, D), dtype=np.float32)
+    elif dtype == "bf16":
+        q = _normal_bf16(r["q"], (B, Hq, N, D))
+        k = _normal_bf16(r["k"], (B, Hkv, N, D))
+        v = _normal_bf16(r["v"], (B, Hkv, N, D))
+    else:
+        raise ValueError(dtype)
+    return PrefillInputs(q=q, k=k, v=v, dtype=dtype, scale=sc)
+
+
+def planted_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, D: int, block: int,
+                   planted_per_mille: int = 50) -> PrefillInputs:
+    """Dense bf16 inputs plus planted high-attention keys.
+
+    Per (batch, kv-head g): choose nKB*planted_per_mille//1000 key blocks j without replacement from
+    [0, nKB-2]. For each: a slot u in [0, block), a later query block i in [j+1, nQB-1], a query row t in block i
+    and a query head h of g's group are drawn, and key row j*block+u of kv-head g is overwritten with
+    bf16(6.0 * q[b, h, t]). The key then scores far above its neighbours for that query while the block's mean
+    barely moves, which is the geometry the mean-dilution section describes."""
+    if N % block:
+        raise ValueError("N must be a multiple of block")
+    inp = dense_inputs(seed, B, Hq, Hkv, N, D, "bf16")
+    inp.block = block
+    rng = streams(seed, ["q", "k", "v", "planted", "rows"])["planted"]
+    nb = N // block
+    G = Hq // Hkv
+    count = nb * planted_per_mille // 1000
+    for b in range(B):
+        for g in range(Hkv):
+            js = rng.choice(nb - 1, size=count, replace=False)
+            for j in sorted(int(x) for x in js):
+                u = int(rng.integers(0, block))
+                i = int(rng.integers(j + 1, nb))
+                t = int(rng.integers(i * block, (i + 1) * block))
+                h = g * G + int(rng.integers(0, G))
+                qv = f32_from_bf16_bits(inp.q[b, h, t])
+                inp.k[b, g, j * block + u] = bf16_bits_from_f32(np.float32(6.0) * qv)
+                inp.planted.append((b, g, j, u, h, t))
+    return inp
+
+
+# --------------------------------------------------------------------------------------------------------------
+# decode inputs
+# --------------------------------------------------------------------------------------------------------------
+@dataclass
+class DecodeInputs:
+    """q [B,Hq,D]; k_cache/v_cache [num_pages,Hkv,page,D] (bf16 bits); block_table [B,max_pages] int32 (-1 pad);
+    seq_lens [B] int32. Slots at or past seq_lens[b] in a sequence's last page hold NaN bit patterns."""
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_table: np.ndarray
+    seq_lens: np.ndarray
+    page: int
+    scale: float
+
+    @property
+    def shape(self) -> Tuple[int, int, int, int]:
+        B, Hq, D = self.q.shape
+        return B, Hq, self.k_cache.shape[1], D
+
+
+def decode_inputs(seed: int, B: int, Hq: int, Hkv: int, D: int, page: int, len_lo: int, len_hi: int,
+                  poison_tail: bool = True, seq_lens: Optional[np.ndarray] = None) -> DecodeInputs:
+    """Paged KV cache with per-sequence lengths uniform on [len_lo, len_hi] (both ends inclusive).
+
+    Physical pages number exactly sum(ceil(L_b / page)); they are handed out from one seeded permutation in
+    sequence order, so logical page p of sequence b lives at block_table[b, p]. Entries past a sequence's last
+    page are -1 and are never meant to be read."""
+    r = streams(seed, ["q", "k", "v", "lens", "perm", "rows"])
+    if seq_lens is None:
+        lens = r["lens"].integers(len_lo, len_hi, size=B, endpoint=True).astype(np.int32)
+    else:
+        lens = np.asarray(seq_lens, dtype=np.int32)
+    pages_per = (lens.astype(np.int64) + page - 1) // page
+    num_pages = int(pages_per.sum())
+    max_pages = max(1, -(-int(len_hi) // page))
+    perm = r["perm"].permutation(num_pages).astype(np.int32)
+    bt = np.full((B, max_pages), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        n = int(pages_per[b])
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    kc = _normal_bf16(r["k"], (max(num_pages, 1), Hkv, page, D))
+    vc = _normal_bf16(r["v"], (max(num_pages, 1), Hkv, page, D))
+    if poison_tail:
+        for b in range(B):
+            L = int(lens[b])
+            if L % page:
+                pid = bt[b, L // page]
+                kc[pid, :, L % page:, :] = BF16_NAN_BITS
+                vc[pid, :, L % page:, :] = BF16_NAN_BITS
+    q = _normal_bf16(r["q"], (B, Hq, D))
+    return DecodeInputs(q=q, k_cache=kc, v_cache=vc, block_table=bt, seq_lens=lens, page=page,
+                        scale=float(1.0 / np.sqrt(D)))
+
+
+# --------------------------------------------------------------------------------------------------------------
+# sampled query rows for large configurations
+# --------------------------------------------------------------------------------------------------------------
+def sample_rows(seed: int, N: int, Hq: int, per_head: int, block: Optional[int] = None,
+                planted: Optional[List[Tuple[int, int, int, int, int, int]]] = None) -> np.ndarray:
+    """Sorted query-row indices per head, int64 [Hq, R] (same R for every head).
+
+    Every head's sample holds row 0, row N-1, the first and last row of a middle block (or of the middle 64
+    rows) and, for planted inputs, the planted query rows of that head; the rest is drawn without
+    replacement."""
+    rng = streams(seed, ["q", "k", "v", "planted", "rows"])["rows"]
+    b = block or 64
+    mid = (N // b // 2) * b
+    fixed = {0, N - 1, min(mid, N - 1), min(mid + b - 1, N - 1)}
+    per_head_fixed = [set(fixed) for _ in range(Hq)]
+    if planted:
+        for (_, _, _, _, h, t) in planted:
+            per_head_fixed[h].add(int(t))
+    R = max(per_head, max(len(s) for s in per_head_fixed))
+    R = min(R, N)
+    out = np.empty((Hq, R), dtype=np.int64)
+    for h in range(Hq):
+        base = sorted(per_head_fixed[h])[:R]
+        need = R - len(base)
+        pool = np.setdiff1d(np.arange(N, dtype=np.int64), np.asarray(base, dtype=np.int64), assume_unique=True) \
+            if N <= (1 << 22) else None
+        if need > 0:
+            if pool is not None:
+                extra = rng.choice(pool, size=need, replace=False)
+            else:
+                extra = set()
+                while len(extra) < need:
+                    for x in rng.integers(0, N, size=need * 2):
+                        if int(x) not in per_head_fixed[h] and len(extra) < need:
+                            extra.add(int(x))
+                extra = np.fromiter(extra, dtype=np.int64)
+            rows = np.concatenate([np.asarray(base, dtype=np.int64), np.asarray(extra, dtype=np.int64)])
+        else:
+            rows = np.asarray(base, dtype=np.int64)
+        out[h] = np.sort(rows)
+    return out
+
+
+# --------------------------------------------------------------------------------------------------------------
+# the named workloads
+# --------------------------------------------------------------------------------------------------------------
+WORKLOADS = {
+    "c1_dense_fp32_n256": dict(kind="dense", seed=1, B=1, Hq=1, Hkv=1, N=256, D=64, dtype="fp32"),
+    "c2_dense_bf16_n4k": dict(kind="dense", seed=2, B=1, Hq=32, Hkv=4, N=4096, D=128, dtype="bf16"),
+    "c3_sparse_bf16_n32k": dict(kind="sparse", seed=3, B=1, Hq=32, Hkv=4, N=32768, D=128, block=64,
+                                keep_permille=100, alpha=1.0, q_lo_pct=50, q_hi_pct=90),
+    "c4_sparse_bf16_n128k": dict(kind="sparse", seed=4, B=1, Hq=32, Hkv=4, N=131072, D=128, block=128,
+                                 keep_permille=50, alpha=1.0, q_lo_pct=50, q_hi_pct=90),
+    "c5_decode_paged_bf16": dict(kind="decode", seed=5, B=32, Hq=64, Hkv=8, D=64, page=16, len_lo=1024,
+                                 len_hi=32768, chunk=512),
+}
+
+
+def make(name: str):
+    """Generate the named workload's inputs."""
+    w = WORKLOADS[name]
+    if w["kind"] == "dense":
+        return dense_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["dtype"])
+    if w["kind"] == "sparse":
+        return planted_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["block"])
+    if w["kind"] == "decode":
+        return decode_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["D"], w["page"], w["len_lo"], w["len_hi"])
+    raise KeyError(name)
