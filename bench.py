@@ -1,0 +1,250 @@
+"""Throughput of the long-context causal attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-long] [--no-cpu-baseline]
+
+A step runs every variant once, each on its own synthetic workload, with inputs already resident in HBM:
+  dense   causal GQA prefill, B1 Hq32 Hkv4 D128 N4096 (the headline workload)
+  sparse  block-mask build + block-sparse prefill, N32768 block 64, centroid budget 10%, rescue alpha 1
+  decode  split-KV paged decode, B32 Hq64 Hkv8 D64, lengths U[1024, 32768], page 16, 512-token chunks
+`value` is the dense prefill's TFLOP/s (causal count 2*B*Hq*N^2*D over the kernel's own event-timed duration).
+After the timed steps the long-context lines are measured on their own: dense prefill at 32K and 128K and the
+128K mask + sparse pass (speedup over this build's dense kernel at the same length). The fp64 CPU oracle is timed
+on the host (cpu_baseline) on the headline workload. One JSON line goes to stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "prefill attention TFLOP/s (dense-equiv) + % bf16 MFMA peak; decode HBM GB/s"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def dense_flops(B, Hq, N, D):
+    return 2.0 * B * Hq * N * N * D
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-long", action="store_true", help="skip the 32K/128K dense and 128K sparse lines")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--long-reps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (each GPU would run an "
+              f"independent share: see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import long_context_attention_causal_amd as lca
+    import workloads as W
+
+    lca.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------------------------------------------------------------------------------- inputs
+    log("generating the headline dense workload (N=4096)")
+    w2 = W.WORKLOADS["c2_dense_bf16_n4k"]
+    c2 = W.make("c2_dense_bf16_n4k")
+    q2, k2, v2 = to_dev(c2.q), to_dev(c2.k), to_dev(c2.v)
+    o2 = torch.empty_like(q2)
+
+    log("generating the 32K block-sparse workload")
+    w3 = W.WORKLOADS["c3_sparse_bf16_n32k"]
+    c3 = W.make("c3_sparse_bf16_n32k")
+    q3, k3, v3 = to_dev(c3.q), to_dev(c3.k), to_dev(c3.v)
+    o3 = torch.empty_like(q3)
+    m3 = lca.block_mask_build(q3, k3, w3["block"], w3["keep_permille"], w3["alpha"], w3["q_lo_pct"], w3["q_hi_pct"],
+                              scale=c3.scale, want_radius_stats=False)
+
+    log("generating the paged decode workload")
+    w5 = W.WORKLOADS["c5_decode_paged_bf16"]
+    c5 = W.make("c5_decode_paged_bf16")
+    q5, kc5, vc5 = to_dev(c5.q), to_dev(c5.k_cache), to_dev(c5.v_cache)
+    bt5 = torch.from_numpy(c5.block_table).to(dev)
+    sl5 = torch.from_numpy(c5.seq_lens).to(dev)
+    maxlen5 = int(w5["len_hi"])
+    o5 = torch.empty_like(q5)
+    ws5 = torch.empty(lca.decode_workspace_bytes(q5, kc5, bt5, maxlen5, w5["chunk"]), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(rec):
+        e = [ev() for _ in range(6)]
+        e[0].record()
+        lca.prefill_dense(q2, k2, v2, scale=c2.scale, out=o2, return_lse=False)
+        e[1].record()
+        lca.block_mask_build(q3, k3, w3["block"], w3["keep_permille"], w3["alpha"], w3["q_lo_pct"], w3["q_hi_pct"],
+                             scale=c3.scale, outputs=m3)
+        e[2].record()
+        lca.prefill_block_sparse(q3, k3, v3, m3.kv_count, m3.kv_index, w3["block"], scale=c3.scale, out=o3,
+                                 return_lse=False)
+        e[3].record()
+        lca.decode_paged(q5, kc5, vc5, bt5, sl5, maxlen5, w5["chunk"], scale=c5.scale, out=o5, return_lse=False,
+                         workspace=ws5)
+        e[4].record()
+        rec.append(e)
+
+    log(f"warmup {args.warmup}, timed {args.steps} steps")
+    junk = []
+    for _ in range(args.warmup):
+        step(junk)
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[r[i].elapsed_time(r[i + 1]) for i in range(4)] for r in recs])   # ms per part
+    t_dense, t_mask3, t_sparse3, t_dec = (float(x) for x in per.mean(axis=0))
+
+    B, Hq, N, D = c2.q.shape
+    fl2 = dense_flops(B, Hq, N, D)
+    tflops2 = fl2 / (t_dense * 1e-3) / 1e12
+
+    # sparse accounting from the mask the GPU built
+    cnt3 = m3.kv_count.cpu().numpy().astype(np.int64)
+    b3 = w3["block"]
+    D3 = w3["D"]
+    exec3 = float(((cnt3 - 1) * 4.0 * b3 * b3 * D3 + 2.0 * b3 * (b3 + 1) * D3).sum())
+    causal_pairs3 = w3["Hq"] * (w3["N"] // b3) * (w3["N"] // b3 + 1) / 2
+    density3 = float(cnt3.sum() / causal_pairs3)
+    dense_eq3 = dense_flops(1, w3["Hq"], w3["N"], D3)
+
+    # decode algorithmic bytes: K and V rows of every cached token, q, o and the block-table entries read
+    L5 = c5.seq_lens.astype(np.int64)
+    Hkv5, D5, Hq5, B5 = w5["Hkv"], w5["D"], w5["Hq"], w5["B"]
+    kv_bytes = float(L5.sum() * Hkv5 * D5 * 2 * 2)
+    dec_bytes = kv_bytes + B5 * Hq5 * D5 * 2 * 2 + float(((L5 + 15) // 16).sum() * 4)
+    dec_gbs = dec_bytes / (t_dec * 1e-3) / 1e9
+
+    # mask stats pass: reads Q and K once
+    mask_read3 = float((w3["Hq"] + w3["Hkv"]) * w3["N"] * D3 * 2)
+
+    paths = {
+        "dense_prefill_n4096": {"ms": t_dense, "tflops": tflops2, "pct_bf16_peak": 100 * tflops2 / PEAK_BF16_TFLOPS,
+                                "tokens_per_s": N / (t_dense * 1e-3)},
+        "mask_build_n32768_b64": {"ms": t_mask3, "stats_read_bytes": mask_read3,
+                                  "stats_read_gbs_over_whole_build": mask_read3 / (t_mask3 * 1e-3) / 1e9,
+                                  "density": density3},
+        "sparse_prefill_n32768_b64": {"ms": t_sparse3, "executed_tflop": exec3 / 1e12,
+                                      "executed_tflops": exec3 / (t_sparse3 * 1e-3) / 1e12,
+                                      "pct_bf16_peak_executed": 100 * exec3 / (t_sparse3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                      "dense_equiv_tflops_incl_mask": dense_eq3 / ((t_sparse3 + t_mask3) * 1e-3) / 1e12},
+        "decode_paged_c5": {"ms": t_dec, "algorithmic_bytes": dec_bytes, "gbs": dec_gbs,
+                            "pct_hbm_peak": 100 * dec_gbs / PEAK_HBM_GBS, "tokens_per_s": B5 / (t_dec * 1e-3),
+                            "tflops": 4.0 * D5 * Hq5 * float(L5.sum()) / (t_dec * 1e-3) / 1e12},
+    }
+
+    def time_calls(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        es = []
+        for _ in range(reps):
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            es.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in es]))
+
+    if not args.no_long:
+        log("dense prefill at 32K")
+        t32 = time_calls(lambda: lca.prefill_dense(q3, k3, v3, scale=c3.scale, out=o3, return_lse=False),
+                         max(args.long_reps, 5))
+        tf32 = dense_eq3 / (t32 * 1e-3) / 1e12
+        paths["dense_prefill_n32768"] = {"ms": t32, "tflops": tf32, "pct_bf16_peak": 100 * tf32 / PEAK_BF16_TFLOPS}
+        paths["sparse_prefill_n32768_b64"]["speedup_vs_dense_kernel_only"] = t32 / t_sparse3
+        paths["sparse_prefill_n32768_b64"]["speedup_vs_dense_incl_mask"] = t32 / (t_sparse3 + t_mask3)
+        del q3, k3, v3, o3, m3
+        torch.cuda.empty_cache()
+        log("generating the 128K block-sparse workload")
+        w4 = W.WORKLOADS["c4_sparse_bf16_n128k"]
+        c4 = W.make("c4_sparse_bf16_n128k")
+        q4, k4, v4 = to_dev(c4.q), to_dev(c4.k), to_dev(c4.v)
+        o4 = torch.empty_like(q4)
+        del c4
+        log("dense prefill at 128K")
+        t128 = time_calls(lambda: lca.prefill_dense(q4, k4, v4, scale=1 / math.sqrt(128), out=o4, return_lse=False),
+                          args.long_reps)
+        fl128 = dense_flops(1, w4["Hq"], w4["N"], w4["D"])
+        tf128 = fl128 / (t128 * 1e-3) / 1e12
+        paths["dense_prefill_n131072"] = {"ms": t128, "tflops": tf128, "pct_bf16_peak": 100 * tf128 / PEAK_BF16_TFLOPS}
+        log("mask build + sparse prefill at 128K")
+        m4 = lca.block_mask_build(q4, k4, w4["block"], w4["keep_permille"], w4["alpha"], w4["q_lo_pct"],
+                                  w4["q_hi_pct"], scale=1 / math.sqrt(128), want_radius_stats=False)
+        tm4 = time_calls(lambda: lca.block_mask_build(q4, k4, w4["block"], w4["keep_permille"], w4["alpha"],
+                                                      w4["q_lo_pct"], w4["q_hi_pct"], scale=1 / math.sqrt(128),
+                                                      outputs=m4), args.long_reps)
+        ts4 = time_calls(lambda: lca.prefill_block_sparse(q4, k4, v4, m4.kv_count, m4.kv_index, w4["block"],
+                                                          scale=1 / math.sqrt(128), out=o4, return_lse=False),
+                         args.long_reps)
+        cnt4 = m4.kv_count.cpu().numpy().astype(np.int64)
+        b4 = w4["block"]
+        exec4 = float(((cnt4 - 1) * 4.0 * b4 * b4 * w4["D"] + 2.0 * b4 * (b4 + 1) * w4["D"]).sum())
+        nb4 = w4["N"] // b4
+        paths["sparse_prefill_n131072_b128"] = {
+            "mask_ms": tm4, "sparse_ms": ts4, "density": float(cnt4.sum() / (w4["Hq"] * nb4 * (nb4 + 1) / 2)),
+            "executed_tflops": exec4 / (ts4 * 1e-3) / 1e12,
+            "pct_bf16_peak_executed": 100 * exec4 / (ts4 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "dense_equiv_tflops_incl_mask": fl128 / ((ts4 + tm4) * 1e-3) / 1e12,
+            "speedup_vs_dense_kernel_only": t128 / ts4,
+            "speedup_vs_dense_incl_mask": t128 / (ts4 + tm4)}
+        del q4, k4, v4, o4, m4
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import attention as A
+        log("timing the fp64 oracle on the host (headline workload, all rows)")
+        qf, kf, vf = c2.as_f64()
+        cores = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        A.causal_attention(qf, kf, vf, c2.scale)
+        tc = time.perf_counter() - t0
+        cpu = {"value": fl2 / tc / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": f"full dense causal GQA prefill B1 Hq32 Hkv4 D128 N4096 in float64 numpy, {tc:.2f} s "
+                         f"(BLAS threads = {os.environ.get('OMP_NUM_THREADS', 'default')})"}
+
+    line = {
+        "metric": METRIC, "value": tflops2, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "c2_dense_bf16_n4k: dense causal GQA prefill B1 Hq32 Hkv4 D128 N4096 "
+                               "(step also runs the N32768 mask+sparse pass and the paged decode)",
+                   "global_batch": 1, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": tflops2, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops2 / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "prefill_dense_bf16_kernel<128, 8>", "per_launch_flop": fl2},
+        "cpu_baseline": cpu,
+        "paths": paths,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

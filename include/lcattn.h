@@ -1,0 +1,166 @@
+/*
+ * lcattn.h -- C ABI of the long-context causal attention library for AMD Instinct MI355X (gfx950).
+ *
+ * Four operations, all exact causal scaled-dot-product attention in the IO-aware tiled form with an online
+ * softmax, so the N x N score matrix never reaches device memory:
+ *
+ *   attn_prefill_dense         causal grouped-query prefill
+ *   attn_block_mask_build      the linear pre-pass that picks key blocks (centroid branch OR radius rescue)
+ *   attn_prefill_block_sparse  prefill restricted to the picked key blocks
+ *   attn_decode_paged          q_len = 1 decode over a paged KV cache, split over KV chunks and reduced by
+ *                              log-sum-exp
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; tensors are dense, row-major in the layouts
+ *     stated per function (last dimension contiguous), and each base pointer is 16-byte aligned.
+ *   - The library never allocates, frees, copies to or from the host, or synchronises. All work is enqueued on
+ *     `stream` (a hipStream_t passed as void*; NULL is the default stream) and runs asynchronously.
+ *   - Arguments are validated on the host before anything is enqueued; a bad argument returns a status and
+ *     enqueues nothing. After enqueueing, a launch failure reported by the HIP runtime returns ATTN_ERR_HIP.
+ *     Faults while a kernel runs surface at the caller's next synchronisation, as with any HIP kernel.
+ *   - attn_last_error() gives a thread-local text for the last non-OK status of the calling thread.
+ *   - Queries are square and top-left aligned: query i attends keys 0..i. Query head h reads key/value head
+ *     h / (heads_q / heads_kv) (contiguous groups).
+ *   - The softmax uses exp(scale * q.k); lse outputs are natural-log log-sum-exps, fp32.
+ */
+#ifndef LCATTN_H
+#define LCATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCATTN_ABI_VERSION 1
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,         /* a required pointer is NULL                                        */
+    ATTN_ERR_SHAPE = 2,        /* inconsistent or out-of-range sizes                                */
+    ATTN_ERR_UNSUPPORTED = 3,  /* valid request this build does not implement (dtype, head_dim ...) */
+    ATTN_ERR_ALIGN = 4,        /* a base pointer is not 16-byte aligned                             */
+    ATTN_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the *_workspace_bytes query        */
+    ATTN_ERR_HIP = 6           /* the HIP runtime reported an error while enqueueing                */
+} attn_status_t;
+
+typedef enum { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype_t;
+
+/* Prefill problem: Q [batch, heads_q, seq_len, head_dim]; K and V [batch, heads_kv, seq_len, head_dim];
+ * O like Q in the same dtype. heads_q must be a multiple of heads_kv; scale must be finite and > 0. */
+typedef struct {
+    int32_t batch, heads_q, heads_kv, seq_len, head_dim;
+    float scale;
+    int32_t dtype; /* attn_dtype_t */
+} attn_shape_t;
+
+/* Block-mask rule parameters ("Your 128K Context Is 6x Slower Than It Needs to Be", section "The rescue
+ * branch: two selection paths, one mask"). */
+typedef struct {
+    int32_t block_size;    /* rows per query block == keys per key block; a multiple of 64                 */
+    int32_t keep_permille; /* centroid budget: row i keeps ceil((i+1) * keep_permille / 1000) blocks, 0..1000 */
+    double rescue_alpha;   /* tau = med + alpha * (p_hi - med); +INF disables the rescue branch, >= 0       */
+    int32_t q_lo_pct;      /* lower reference percentile of the radii (50 = median), 0..100                */
+    int32_t q_hi_pct;      /* upper reference percentile (90), q_lo_pct <= q_hi_pct <= 100                 */
+} attn_mask_params_t;
+
+/* Decode problem: q [batch, heads_q, head_dim]; caches [num_pages, heads_kv, page_size, head_dim];
+ * block_table [batch, max_pages_per_seq] int32; seq_lens [batch] int32; O [batch, heads_q, head_dim]. */
+typedef struct {
+    int32_t batch, heads_q, heads_kv, head_dim, page_size, max_pages_per_seq, num_pages, chunk_tokens;
+    float scale;
+} attn_decode_shape_t;
+
+/*
+ * Dense causal GQA prefill ("attention-kernel-optimization", section "FlashAttention (1 -> 2 -> 3)": tiles of
+ * Q, K, V on chip, online-normalised softmax, O(N d) memory).
+ *   q, k, v  inputs in shape->dtype (bf16 or fp32), layouts as attn_shape_t.
+ *   o        output, same dtype and layout as q.
+ *   lse      optional fp32 [batch, heads_q, seq_len] (NULL to skip).
+ * Supported: head_dim 64 or 128; bf16 (MFMA, fp32 accumulation) or fp32 (fp32 arithmetic throughout).
+ * seq_len 0 is a no-op.
+ */
+attn_status_t attn_prefill_dense(const attn_shape_t* shape, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, void* stream);
+
+/* Bytes of device workspace attn_block_mask_build needs for this shape and block size (0 on bad input). */
+size_t attn_block_mask_workspace_bytes(const attn_shape_t* shape, const attn_mask_params_t* params);
+
+/*
+ * The block-selection pre-pass ("Your 128K Context Is 6x Slower Than It Needs to Be", sections "Why
+ * block-sparse attention underperforms: the mean-dilution trap" and "The rescue branch"), with nb =
+ * seq_len / block_size query blocks and as many key blocks:
+ *   1. per query head and query block, the mean of the block's query rows; per kv head and key block, the key
+ *      centroid and the radius (largest Euclidean key-to-centroid distance); float64, one pass over Q and K;
+ *   2. per (batch, kv head): type-7 (linear) quantiles of the radii at q_lo_pct and q_hi_pct, and
+ *      tau = med + alpha * (p_hi - med);
+ *   3. rescue flag of key block j: radius_j > tau (strict), shared by the kv head's query heads;
+ *   4. centroid branch of row (h, i): among key blocks j <= i, the ceil((i+1) * keep_permille / 1000) largest
+ *      scale * <query-block mean, key centroid> (float64), ties to the smaller j;
+ *   5. mask[h,i,j] = 1 iff j <= i and (centroid pick or rescue flag or j == i).
+ * Inputs: q, k bf16 in the prefill layouts. Outputs:
+ *   mask      uint8 [batch, heads_q, nb, nb], 0/1, written in full.
+ *   kv_count  int32 [batch, heads_q, nb], number of kept blocks per row.
+ *   kv_index  int32 [batch, heads_q, nb, nb], kept key blocks of each row in ascending order in the first
+ *             kv_count entries; later entries are not written.
+ *   radius_stats  optional float64 [batch, heads_kv, nb + 3]: the nb radii, then med, p_hi, tau (NULL to skip).
+ * Workspace (>= attn_block_mask_workspace_bytes, 256-byte aligned) holds, in order and each 256-byte aligned:
+ * query-block means f64 [batch, heads_q, nb, head_dim], key centroids f64 [batch, heads_kv, nb, head_dim],
+ * radii f64 [batch, heads_kv, nb], (med, p_hi, tau, 0) f64 [batch, heads_kv, 4], rescue flags u8
+ * [batch, heads_kv, nb], centroid scores f64 [batch, heads_q, nb, nb] (lower triangle only).
+ * Supported: bf16, head_dim 64 or 128, block_size a multiple of 64 dividing seq_len, 1 <= nb <= 4096.
+ */
+attn_status_t attn_block_mask_build(const attn_shape_t* shape, const attn_mask_params_t* params, const void* q,
+                                    const void* k, uint8_t* mask, int32_t* kv_count, int32_t* kv_index,
+                                    double* radius_stats, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse causal prefill: dense prefill restricted, for query row t of query block i = t / block_size, to
+ * the keys u <= t whose key block u / block_size is listed in kv_index[b, h, i, 0 .. kv_count[b,h,i]) ("Your
+ * 128K Context Is 6x Slower Than It Needs to Be", sections "Why block-sparse attention underperforms" and "The
+ * rescue branch": the combined mask runs as ordinary block-sparse tiled attention and skipped blocks cost
+ * nothing). Lists must be ascending, within [0, i], and hold i itself (every row then sees at least its own
+ * key); the kernel trusts them, so the caller validates untrusted lists. kv_count/kv_index as produced by
+ * attn_block_mask_build. Supported: bf16, head_dim 64 or 128, block_size a multiple of 64 dividing seq_len.
+ */
+attn_status_t attn_prefill_block_sparse(const attn_shape_t* shape, int32_t block_size, const void* q,
+                                        const void* k, const void* v, const int32_t* kv_count,
+                                        const int32_t* kv_index, void* o, float* lse, void* stream);
+
+/* Bytes of device workspace attn_decode_paged needs when no sequence is longer than max_seq_len. */
+size_t attn_decode_workspace_bytes(const attn_decode_shape_t* shape, int32_t max_seq_len);
+
+/*
+ * Split-KV decode over a paged KV cache ("attention-kernel-optimization", sections "Inference-specific:
+ * Flash-Decoding and FlashInfer" -- split the keys, attend the pieces in parallel, reduce -- and
+ * "PagedAttention" -- fixed-size pages placed anywhere, found through a block table).
+ * The query of sequence b is the token at position seq_lens[b] - 1; it attends all seq_lens[b] cached tokens
+ * (the caller has already written its own K/V). Token t of sequence b sits in slot t % page_size of page
+ * block_table[b, t / page_size]. Each work-group takes chunk_tokens tokens of one (sequence, kv head) for all
+ * heads_q / heads_kv query heads; a second kernel merges the chunks by log-sum-exp.
+ *   q         bf16 [batch, heads_q, head_dim]
+ *   k_cache, v_cache  bf16 [num_pages, heads_kv, page_size, head_dim]
+ *   block_table  int32 [batch, max_pages_per_seq]; only entries < ceil(seq_lens[b] / page_size) are read and
+ *             each must lie in [0, num_pages) (trusted, not checked on the device).
+ *   seq_lens  int32 [batch], each in [0, max_seq_len] (trusted, not checked on the device).
+ *   max_seq_len  host-side upper bound of seq_lens, sizes the grid and the workspace.
+ *   o         bf16 [batch, heads_q, head_dim]; lse optional fp32 [batch, heads_q] (NULL to skip).
+ * Cache slots at or past seq_lens[b] and pages the table does not reference may hold any bits, NaN included;
+ * they never reach the output. seq_lens[b] == 0 gives o = 0 and lse = -inf.
+ * Supported: head_dim 64 or 128, page_size 16, chunk_tokens a multiple of 64, heads_q / heads_kv <= 16.
+ */
+attn_status_t attn_decode_paged(const attn_decode_shape_t* shape, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                                int32_t max_seq_len, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+const char* attn_status_string(attn_status_t status);
+const char* attn_last_error(void);
+int32_t attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCATTN_H */

@@ -1,0 +1,68 @@
+// Host-side interface between the C ABI layer (abi.hip) and the kernel translation units. Arguments reaching
+// these launchers have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lcattn {
+
+struct PrefillProblem {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;  // may be null
+    int B, Hq, Hkv, N, D;
+    float scale;
+};
+
+hipError_t launch_prefill_dense_bf16(const PrefillProblem& p, hipStream_t s);
+hipError_t launch_prefill_dense_f32(const PrefillProblem& p, hipStream_t s);
+hipError_t launch_prefill_sparse_bf16(const PrefillProblem& p, int block, const int32_t* kv_count,
+                                      const int32_t* kv_index, hipStream_t s);
+
+struct MaskProblem {
+    const void* q;
+    const void* k;
+    int B, Hq, Hkv, N, D, block, nb;
+    double scale;
+    int keep_permille;
+    double alpha;
+    int lo_pct, hi_pct;
+    uint8_t* mask;
+    int32_t* kv_count;
+    int32_t* kv_index;
+    double* radius_stats;  // may be null
+};
+
+struct MaskWorkspace {
+    double* qbar;
+    double* kbar;
+    double* radius;
+    double* thresh;
+    uint8_t* flags;
+    double* scores;
+    size_t total;
+};
+
+MaskWorkspace mask_workspace_layout(int B, int Hq, int Hkv, int nb, int D, char* base);
+hipError_t launch_block_mask(const MaskProblem& p, const MaskWorkspace& ws, hipStream_t s);
+
+struct DecodeProblem {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    void* o;
+    float* lse;  // may be null
+    int B, Hq, Hkv, D, page, max_pages, num_pages, chunk, max_seq_len;
+    float scale;
+};
+
+size_t decode_workspace_bytes(int B, int Hq, int D, int chunk, int max_seq_len);
+hipError_t launch_decode_paged(const DecodeProblem& p, void* workspace, hipStream_t s);
+
+}  // namespace lcattn

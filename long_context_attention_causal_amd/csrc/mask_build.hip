@@ -1,0 +1,441 @@
+// Block-selection pre-pass for gfx950, all arithmetic in float64.
+//
+// Source: "Your 128K Context Is 6x Slower Than It Needs to Be", sections "Why block-sparse attention
+// underperforms: the mean-dilution trap" (a block scored by its key centroid hides a single strong key) and
+// "The rescue branch: two selection paths, one mask" (per key block the largest key-to-centroid distance; a
+// threshold from the median and 90th percentile of those radii per kv head; the two branches thresholded on
+// their own and OR-ed; the pre-pass is linear in sequence length).
+//
+// Four kernels on the caller's stream:
+//   stats     one work-group per query block (mean of its rows) or key block (centroid, then radius): a
+//             coalesced pass over Q and K with 16-byte loads, fp64 sums. The block sums of bf16 values are
+//             exact in fp64 for ordinary data, so the means do not depend on summation order.
+//   threshold one work-group per (batch, kv head): the needed order statistics of the radii by exact rank
+//             counting, then type-7 interpolation and tau, evaluated in the same operation order as the
+//             reference definition with contraction disabled; then the rescue flags.
+//   scores    fp64 tiled product of the query-block means with the key centroids of the same kv head, lower
+//             triangle only (the O(nb^2) block score matrix the page warns about lives in the workspace).
+//   select    one wave per (batch, head, query block): the integer budget, top-k by a bitwise search over
+//             order-preserving 64-bit keys of the scores (ties to the smaller block index), OR with rescue
+//             flags and the diagonal, then the uint8 row and its ascending CSR list via ballots.
+#include <cmath>
+
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace lcattn {
+namespace {
+
+__device__ __forceinline__ double bf16_to_f64(uint32_t bits16) { return (double)bf16_to_f32(bits16); }
+
+struct StatsArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    double* qbar;
+    double* kbar;
+    double* radius;
+    int B, Hq, Hkv, N, block, nb;
+    long nq_blocks;  // B * Hq * nb
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void mask_stats_kernel(const StatsArgs a) {
+    constexpr int CPR = D / 8;        // 16-byte chunks per row
+    constexpr int RPP = 256 / CPR;    // rows per pass
+    __shared__ double part[RPP][D];
+    __shared__ double cen[D];
+    __shared__ double wmax[4];
+    const int tid = threadIdx.x, c = tid % CPR, r0 = tid / CPR;
+    long id = blockIdx.x;
+    const bool isq = id < a.nq_blocks;
+    const uint16_t* base;
+    double* out;
+    int b, hh, j;
+    if (isq) {
+        j = (int)(id % a.nb);
+        const long bh = id / a.nb;
+        hh = (int)(bh % a.Hq);
+        b = (int)(bh / a.Hq);
+        base = a.q + (((size_t)b * a.Hq + hh) * a.N + (size_t)j * a.block) * D;
+        out = a.qbar + (((size_t)b * a.Hq + hh) * a.nb + j) * D;
+    } else {
+        id -= a.nq_blocks;
+        j = (int)(id % a.nb);
+        const long bg = id / a.nb;
+        hh = (int)(bg % a.Hkv);
+        b = (int)(bg / a.Hkv);
+        base = a.k + (((size_t)b * a.Hkv + hh) * a.N + (size_t)j * a.block) * D;
+        out = a.kbar + (((size_t)b * a.Hkv + hh) * a.nb + j) * D;
+    }
+    double s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = 0.0;
+    for (int r = r0; r < a.block; r += RPP) {
+        const u32x4 v = load16(base + (size_t)r * D + c * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += bf16_to_f64((v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[r0][c * 8 + e] = s[e];
+    __syncthreads();
+    if (tid < D) {
+        double t = 0.0;
+        for (int r = 0; r < RPP; ++r) t += part[r][tid];
+        const double mean = t / (double)a.block;
+        out[tid] = mean;
+        cen[tid] = mean;
+    }
+    if (isq) return;  // uniform over the work-group
+    __syncthreads();
+    double cc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cc[e] = cen[c * 8 + e];
+    double best = 0.0;
+    for (int r = r0; r < a.block; r += RPP) {
+        const u32x4 v = load16(base + (size_t)r * D + c * 8);
+        double d2 = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double x = bf16_to_f64((v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu) - cc[e];
+            d2 += x * x;
+        }
+#pragma unroll
+        for (int o = 1; o < CPR; o <<= 1) d2 += __shfl_xor(d2, o);   // the row's CPR lanes are adjacent
+        best = fmax(best, d2);
+    }
+    best = wave_max_f64(best);
+    if ((tid & 63) == 0) wmax[tid >> 6] = best;
+    __syncthreads();
+    if (tid == 0) {
+        const double m = fmax(fmax(wmax[0], wmax[1]), fmax(wmax[2], wmax[3]));
+        a.radius[((size_t)b * a.Hkv + hh) * a.nb + j] = sqrt(m);
+    }
+}
+
+struct ThreshArgs {
+    const double* radius;
+    double* thresh;       // [B*Hkv][4]
+    uint8_t* flags;       // [B*Hkv][nb]
+    double* radius_stats; // optional [B*Hkv][nb+3]
+    int nb, lo_pct, hi_pct;
+    double alpha;
+};
+
+// Type-7 quantile value from the two order statistics around the position, in the reference operation order.
+__device__ double interp7(double xlo, double xhi, long num, bool has_next) {
+#pragma clang fp contract(off)
+    const double f = (double)(num % 100) / 100.0;
+    if (!has_next || f == 0.0) return xlo;
+    return xlo + f * (xhi - xlo);
+}
+
+__global__ __launch_bounds__(1024) void mask_threshold_kernel(const ThreshArgs a) {
+#pragma clang fp contract(off)
+    __shared__ double rs[4096];
+    __shared__ double os[4];
+    const int bg = blockIdx.x, tid = threadIdx.x, n = a.nb;
+    const double* r = a.radius + (size_t)bg * n;
+    for (int e = tid; e < n; e += 1024) rs[e] = r[e];
+    if (tid < 4) os[tid] = 0.0;
+    __syncthreads();
+    const long num_lo = (long)(n - 1) * a.lo_pct, num_hi = (long)(n - 1) * a.hi_pct;
+    const int want[4] = {(int)(num_lo / 100), (int)min((long)n - 1, num_lo / 100 + 1), (int)(num_hi / 100),
+                         (int)min((long)n - 1, num_hi / 100 + 1)};
+    for (int e = tid; e < n; e += 1024) {
+        const double x = rs[e];
+        int lt = 0, le = 0;
+        for (int t = 0; t < n; ++t) {
+            const double y = rs[t];
+            lt += (y < x);
+            le += (y <= x);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (lt <= want[k] && want[k] < le) os[k] = x;  // every writer of a slot writes the same value
+    }
+    __syncthreads();
+    __shared__ double tau_s;
+    if (tid == 0) {
+        const double med = interp7(os[0], os[1], num_lo, num_lo / 100 + 1 < n);
+        const double hi = interp7(os[2], os[3], num_hi, num_hi / 100 + 1 < n);
+        const double tau = isinf(a.alpha) ? INFINITY : med + a.alpha * (hi - med);
+        double* t = a.thresh + (size_t)bg * 4;
+        t[0] = med;
+        t[1] = hi;
+        t[2] = tau;
+        t[3] = 0.0;
+        if (a.radius_stats) {
+            double* rsd = a.radius_stats + (size_t)bg * (n + 3);
+            rsd[n] = med;
+            rsd[n + 1] = hi;
+            rsd[n + 2] = tau;
+        }
+        tau_s = tau;
+    }
+    __syncthreads();
+    const double tau = tau_s;
+    for (int e = tid; e < n; e += 1024) {
+        a.flags[(size_t)bg * n + e] = rs[e] > tau ? 1 : 0;
+        if (a.radius_stats) a.radius_stats[(size_t)bg * (n + 3) + e] = rs[e];
+    }
+}
+
+struct ScoreArgs {
+    const double* qbar;
+    const double* kbar;
+    double* scores;   // [B, Hq, nb, nb]
+    int Hq, Hkv, G, nb, D;
+    double scale;
+};
+
+// 64x64 output tile per work-group, 4x4 per thread, head dim in chunks of 16 through LDS.
+__global__ __launch_bounds__(256) void mask_scores_kernel(const ScoreArgs a) {
+    __shared__ double As[16][65];
+    __shared__ double Bs[16][65];
+    const int tid = threadIdx.x, tr = tid / 16, tc = tid % 16;
+    const int j0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+    const int bg = blockIdx.z, b = bg / a.Hkv, g = bg % a.Hkv;
+    const int R = a.G * a.nb;
+    // rows r = hl * nb + i of the kv head's query heads; skip tiles entirely above the diagonal
+    const int rl = min(r0 + 63, R - 1);
+    const int imax = (r0 / a.nb == rl / a.nb) ? rl % a.nb : a.nb - 1;
+    if (j0 > imax) return;
+    const double* kb = a.kbar + ((size_t)b * a.Hkv + g) * a.nb * a.D;
+    double acc[4][4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+    for (int d0 = 0; d0 < a.D; d0 += 16) {
+        __syncthreads();
+        for (int e = tid; e < 16 * 64; e += 256) {
+            const int rr = e / 16, dd = e % 16;
+            const int r = r0 + rr, j = j0 + rr;
+            double av = 0.0, bv = 0.0;
+            if (r < R) {
+                const int hl = r / a.nb, i = r % a.nb;
+                av = a.qbar[(((size_t)b * a.Hq + g * a.G + hl) * a.nb + i) * a.D + d0 + dd];
+            }
+            if (j < a.nb) bv = kb[(size_t)j * a.D + d0 + dd];
+            As[dd][rr] = av;
+            Bs[dd][rr] = bv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int dd = 0; dd < 16; ++dd) {
+            double x[4], y[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                x[u] = As[dd][tr * 4 + u];
+                y[u] = Bs[dd][tc * 4 + u];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] = fma(x[u], y[v], acc[u][v]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = r0 + tr * 4 + u;
+        if (r >= R) continue;
+        const int hl = r / a.nb, i = r % a.nb;
+        double* srow = a.scores + (((size_t)b * a.Hq + g * a.G + hl) * a.nb + i) * a.nb;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int j = j0 + tc * 4 + v;
+            if (j <= i && j < a.nb) srow[j] = __dmul_rn(a.scale, acc[u][v]);
+        }
+    }
+}
+
+struct SelectArgs {
+    const double* scores;
+    const uint8_t* flags;
+    uint8_t* mask;
+    int32_t* kv_count;
+    int32_t* kv_index;
+    int B, Hq, Hkv, G, nb, keep;
+};
+
+// Order-preserving map of a double onto uint64 (after folding -0 onto +0, which compares equal).
+__device__ __forceinline__ uint64_t order_key(double x) {
+    if (x == 0.0) x = 0.0;
+    const uint64_t u = __double_as_longlong(x);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void mask_select_kernel(const SelectArgs a) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long row = (long)blockIdx.x * 4 + w;
+    if (row >= (long)a.B * a.Hq * a.nb) return;   // no barriers in this kernel
+    const int i = (int)(row % a.nb);
+    const long bh = row / a.nb;
+    const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+    const int g = h / a.G;
+    const double* srow = a.scores + (size_t)row * a.nb;
+    const uint8_t* fl = a.flags + ((size_t)b * a.Hkv + g) * a.nb;
+    const int cand = i + 1;
+    const int budget = min(cand, (int)(((long)cand * a.keep + 999) / 1000));
+    uint64_t key[E];
+    bool kept[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int j = lane + 64 * e;
+        key[e] = j <= i ? order_key(srow[j]) : 0ull;
+        kept[e] = false;
+    }
+    if (budget >= cand) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) kept[e] = (lane + 64 * e) <= i;
+    } else if (budget > 0) {
+        uint64_t T = 0;
+        bool exact = false;
+        for (int bit = 63; bit >= 0; --bit) {
+            const uint64_t c = T | (1ull << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) cnt += __popcll(__ballot((lane + 64 * e) <= i && key[e] >= c));
+            if (cnt >= budget) {
+                T = c;
+                if (cnt == budget) {
+                    exact = true;
+                    break;
+                }
+            }
+        }
+        if (exact) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) kept[e] = (lane + 64 * e) <= i && key[e] >= T;
+        } else {
+            // T is the budget-th largest key and is shared by several candidates: take all above it, then the
+            // tied ones in ascending block order until the budget is met
+            int have = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                kept[e] = (lane + 64 * e) <= i && key[e] > T;
+                have += __popcll(__ballot(kept[e]));
+            }
+            int need = budget - have;
+            const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bool tie = (lane + 64 * e) <= i && key[e] == T;
+                const uint64_t bal = __ballot(tie);
+                const int before = __popcll(bal & below);
+                if (tie && before < need) kept[e] = true;
+                need -= min(need, __popcll(bal));
+            }
+        }
+    }
+    uint8_t* mrow = a.mask + (size_t)row * a.nb;
+    int32_t* irow = a.kv_index + (size_t)row * a.nb;
+    const uint64_t below = (1ull << lane) - 1ull;
+    int count = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int j = lane + 64 * e;
+        const bool m = j <= i && (kept[e] || fl[j] != 0 || j == i);
+        if (j < a.nb) mrow[j] = m ? 1 : 0;
+        const uint64_t bal = __ballot(m);
+        if (m) irow[count + __popcll(bal & below)] = j;
+        count += __popcll(bal);
+    }
+    if (lane == 0) a.kv_count[row] = count;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+MaskWorkspace mask_workspace_layout(int B, int Hq, int Hkv, int nb, int D, char* base) {
+    MaskWorkspace w;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + off : nullptr;
+        off += align256(bytes);
+        return p;
+    };
+    w.qbar = reinterpret_cast<double*>(take((size_t)B * Hq * nb * D * 8));
+    w.kbar = reinterpret_cast<double*>(take((size_t)B * Hkv * nb * D * 8));
+    w.radius = reinterpret_cast<double*>(take((size_t)B * Hkv * nb * 8));
+    w.thresh = reinterpret_cast<double*>(take((size_t)B * Hkv * 4 * 8));
+    w.flags = reinterpret_cast<uint8_t*>(take((size_t)B * Hkv * nb));
+    w.scores = reinterpret_cast<double*>(take((size_t)B * Hq * nb * nb * 8));
+    w.total = off;
+    return w;
+}
+
+hipError_t launch_block_mask(const MaskProblem& p, const MaskWorkspace& ws, hipStream_t s) {
+    StatsArgs sa;
+    sa.q = static_cast<const uint16_t*>(p.q);
+    sa.k = static_cast<const uint16_t*>(p.k);
+    sa.qbar = ws.qbar;
+    sa.kbar = ws.kbar;
+    sa.radius = ws.radius;
+    sa.B = p.B;
+    sa.Hq = p.Hq;
+    sa.Hkv = p.Hkv;
+    sa.N = p.N;
+    sa.block = p.block;
+    sa.nb = p.nb;
+    sa.nq_blocks = (long)p.B * p.Hq * p.nb;
+    const unsigned nstat = (unsigned)(sa.nq_blocks + (long)p.B * p.Hkv * p.nb);
+    if (p.D == 128) hipLaunchKernelGGL((mask_stats_kernel<128>), dim3(nstat), dim3(256), 0, s, sa);
+    else hipLaunchKernelGGL((mask_stats_kernel<64>), dim3(nstat), dim3(256), 0, s, sa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    ThreshArgs ta;
+    ta.radius = ws.radius;
+    ta.thresh = ws.thresh;
+    ta.flags = ws.flags;
+    ta.radius_stats = p.radius_stats;
+    ta.nb = p.nb;
+    ta.lo_pct = p.lo_pct;
+    ta.hi_pct = p.hi_pct;
+    ta.alpha = p.alpha;
+    hipLaunchKernelGGL(mask_threshold_kernel, dim3((unsigned)(p.B * p.Hkv)), dim3(1024), 0, s, ta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    ScoreArgs sc;
+    sc.qbar = ws.qbar;
+    sc.kbar = ws.kbar;
+    sc.scores = ws.scores;
+    sc.Hq = p.Hq;
+    sc.Hkv = p.Hkv;
+    sc.G = p.Hq / p.Hkv;
+    sc.nb = p.nb;
+    sc.D = p.D;
+    sc.scale = p.scale;
+    const dim3 sgrid((unsigned)((p.nb + 63) / 64), (unsigned)((sc.G * p.nb + 63) / 64), (unsigned)(p.B * p.Hkv));
+    hipLaunchKernelGGL(mask_scores_kernel, sgrid, dim3(256), 0, s, sc);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    SelectArgs se;
+    se.scores = ws.scores;
+    se.flags = ws.flags;
+    se.mask = p.mask;
+    se.kv_count = p.kv_count;
+    se.kv_index = p.kv_index;
+    se.B = p.B;
+    se.Hq = p.Hq;
+    se.Hkv = p.Hkv;
+    se.G = p.Hq / p.Hkv;
+    se.nb = p.nb;
+    se.keep = p.keep_permille;
+    const long rows = (long)p.B * p.Hq * p.nb;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    const int E = (p.nb + 63) / 64;
+    if (E <= 1) hipLaunchKernelGGL((mask_select_kernel<1>), grid, dim3(256), 0, s, se);
+    else if (E <= 2) hipLaunchKernelGGL((mask_select_kernel<2>), grid, dim3(256), 0, s, se);
+    else if (E <= 4) hipLaunchKernelGGL((mask_select_kernel<4>), grid, dim3(256), 0, s, se);
+    else if (E <= 8) hipLaunchKernelGGL((mask_select_kernel<8>), grid, dim3(256), 0, s, se);
+    else if (E <= 16) hipLaunchKernelGGL((mask_select_kernel<16>), grid, dim3(256), 0, s, se);
+    else if (E <= 32) hipLaunchKernelGGL((mask_select_kernel<32>), grid, dim3(256), 0, s, se);
+    else hipLaunchKernelGGL((mask_select_kernel<64>), grid, dim3(256), 0, s, se);
+    return hipGetLastError();
+}
+
+}  // namespace lcattn

@@ -1,0 +1,170 @@
+"""The C ABI without a GPU: the library loads, exports what include/lcattn.h declares, sizes workspaces, and
+rejects bad arguments on the host before enqueueing anything. No call here reaches a kernel launch: every
+argument set is invalid, or the problem is empty."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import long_context_attention_causal_amd as lca
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lcattn.h")
+FAKE = 1 << 20          # aligned, non-null, never dereferenced: validation fails before any launch
+MISALIGNED = FAKE + 4
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lca.LIB_PATH):
+        from long_context_attention_causal_amd import build
+        build.build(verbose=False)
+    return lca.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:attn_status_t|size_t|const char\*|int32_t)\s+(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_function(L):
+    decl = declared_functions()
+    assert len(decl) == 9
+    for name in decl:
+        assert hasattr(L, name), name
+    assert set(decl) == set(lca.EXPORTS)
+
+
+def test_version_and_status_strings(L):
+    assert lca.abi_version() == 1
+    for st in range(7):
+        assert L.attn_status_string(st)
+    assert L.attn_status_string(99) == b"unknown status"
+
+
+def shape(B=1, Hq=4, Hkv=2, N=128, D=128, scale=0.1, dtype=0):
+    return lca.AttnShape(B, Hq, Hkv, N, D, scale, dtype)
+
+
+def dense(L, s, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None):
+    return L.attn_prefill_dense(ctypes.byref(s) if s is not None else None, q, k, v, o, lse, None)
+
+
+@pytest.mark.parametrize("s,code", [
+    (None, 1),
+    (shape(Hq=3, Hkv=2), 2),
+    (shape(D=96), 3),
+    (shape(scale=0.0), 2),
+    (shape(scale=math.inf), 2),
+    (shape(dtype=7), 3),
+    (shape(B=0), 2),
+    (shape(N=-1), 2),
+])
+def test_prefill_dense_rejects(L, s, code):
+    assert dense(L, s) == code
+    assert L.attn_last_error()
+
+
+def test_prefill_dense_pointer_checks(L):
+    assert dense(L, shape(), q=None) == 1
+    assert dense(L, shape(), v=MISALIGNED) == 4
+    assert dense(L, shape(), lse=MISALIGNED) == 4
+    assert dense(L, shape(N=0), q=None) == 0      # empty problem: nothing to do, nothing read
+
+
+def params(block=64, keep=100, alpha=1.0, lo=50, hi=90):
+    return lca.AttnMaskParams(block, keep, alpha, lo, hi)
+
+
+@pytest.mark.parametrize("s,p,code", [
+    (shape(dtype=1), params(), 3),
+    (shape(N=100), params(), 2),
+    (shape(), params(block=32), 3),
+    (shape(), params(keep=1001), 2),
+    (shape(), params(alpha=-1.0), 2),
+    (shape(), params(alpha=math.nan), 2),
+    (shape(), params(lo=90, hi=50), 2),
+    (shape(N=64 * 5000), params(), 3),
+])
+def test_mask_build_rejects(L, s, p, code):
+    assert L.attn_block_mask_workspace_bytes(ctypes.byref(s), ctypes.byref(p)) == 0
+    assert L.attn_block_mask_build(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                   1 << 40, None) == code
+
+
+def test_mask_workspace_size_and_check(L):
+    B, Hq, Hkv, N, D, blk = 2, 8, 2, 512, 128, 64
+    nb = N // blk
+    s, p = shape(B, Hq, Hkv, N, D), params(blk)
+    need = L.attn_block_mask_workspace_bytes(ctypes.byref(s), ctypes.byref(p))
+    a = lambda x: (x + 255) // 256 * 256
+    want = (a(B * Hq * nb * D * 8) + a(B * Hkv * nb * D * 8) + a(B * Hkv * nb * 8) + a(B * Hkv * 32)
+            + a(B * Hkv * nb) + a(B * Hq * nb * nb * 8))
+    assert need == want
+    assert L.attn_block_mask_build(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                   need - 1, None) == 5
+    assert L.attn_block_mask_build(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                   need, None) == 5
+    assert L.attn_block_mask_build(ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                   FAKE + 16, need, None) == 4
+    assert L.attn_block_mask_build(ctypes.byref(s), ctypes.byref(p), FAKE, None, FAKE, FAKE, FAKE, None, FAKE,
+                                   need, None) == 1
+
+
+@pytest.mark.parametrize("blk,N,code", [(32, 128, 3), (64, 100, 2), (512, 1024, 3)])
+def test_sparse_rejects(L, blk, N, code):
+    s = shape(N=N)
+    assert L.attn_prefill_block_sparse(ctypes.byref(s), blk, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == code
+
+
+def test_sparse_pointer_checks(L):
+    s = shape()
+    assert L.attn_prefill_block_sparse(ctypes.byref(s), 64, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None) == 1
+    assert L.attn_prefill_block_sparse(ctypes.byref(s), 64, FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE, None,
+                                       None) == 4
+    fp32 = shape(dtype=1)
+    assert L.attn_prefill_block_sparse(ctypes.byref(fp32), 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 3
+
+
+def dshape(B=4, Hq=16, Hkv=2, D=64, page=16, maxp=64, pages=100, chunk=512, scale=0.125):
+    return lca.AttnDecodeShape(B, Hq, Hkv, D, page, maxp, pages, chunk, scale)
+
+
+@pytest.mark.parametrize("s,maxlen,code", [
+    (dshape(Hq=15), 100, 2),
+    (dshape(Hq=64, Hkv=2), 100, 3),
+    (dshape(D=80), 100, 3),
+    (dshape(page=32), 100, 3),
+    (dshape(chunk=500), 100, 3),
+    (dshape(), 64 * 16 + 1, 2),
+    (dshape(), -1, 2),
+    (dshape(scale=-1.0), 100, 2),
+    (dshape(pages=0), 100, 2),
+])
+def test_decode_rejects(L, s, maxlen, code):
+    assert L.attn_decode_paged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, maxlen, FAKE, None, FAKE, 1 << 40,
+                               None) == code
+
+
+def test_decode_workspace(L):
+    s = dshape()
+    need = L.attn_decode_workspace_bytes(ctypes.byref(s), 1000)
+    C = -(-1000 // 512)
+    a = lambda x: (x + 255) // 256 * 256
+    assert need == a(4 * 16 * C * 64 * 4) + a(4 * 16 * C * 4)
+    assert L.attn_decode_paged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, 1000, FAKE, None, FAKE, need - 1,
+                               None) == 5
+    assert L.attn_decode_paged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, 1000, FAKE, None, FAKE + 64, need,
+                               None) == 4
+    assert L.attn_decode_paged(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, 1000, FAKE, None, FAKE, need,
+                               None) == 1
+    assert L.attn_decode_workspace_bytes(ctypes.byref(dshape(page=8)), 1000) == 0
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(lca.LcattnError):
+        lca.prefill_dense(q, q[:, :1].contiguous(), q[:, :1].contiguous())

@@ -1,0 +1,105 @@
+"""GPU parity of attn_decode_paged against the fp64 oracle, plus element-exact gather probes."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as A
+from tests.gpu_util import BF16_TOL, LSE_TOL, dev_bf16, dev_i32, host64, max_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def to_dev(d: W.DecodeInputs):
+    return (dev_bf16(d.q), dev_bf16(d.k_cache), dev_bf16(d.v_cache), dev_i32(d.block_table), dev_i32(d.seq_lens))
+
+
+def oracle(d: W.DecodeInputs):
+    return A.paged_decode(W.f64_from_bf16_bits(d.q), W.f64_from_bf16_bits(d.k_cache),
+                          W.f64_from_bf16_bits(d.v_cache), d.block_table, d.seq_lens, d.scale)
+
+
+def run(lib, d, chunk=512, max_len=None):
+    q, kc, vc, bt, sl = to_dev(d)
+    ml = int(d.seq_lens.max()) if max_len is None else max_len
+    o, lse = lib.decode_paged(q, kc, vc, bt, sl, ml, chunk_tokens=chunk, scale=d.scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def compare(lib, d, label, chunk=512):
+    o, lse = run(lib, d, chunk)
+    Oref, Lref = oracle(d)
+    og, lg = host64(o), host64(lse)
+    live = d.seq_lens > 0
+    eo = max_err(og, Oref)
+    el = max_err(lg[live], Lref[live])
+    say(f"[decode] {label} chunk={chunk} max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert np.isfinite(og).all()
+    assert eo <= BF16_TOL and el <= LSE_TOL
+    if (~live).any():
+        assert (og[~live] == 0).all() and np.isneginf(lg[~live]).all()
+    return o, lse
+
+
+def test_c5_full(lib):
+    w = W.WORKLOADS["c5_decode_paged_bf16"]
+    say("[decode] c5: generating inputs")
+    d = W.make("c5_decode_paged_bf16")
+    compare(lib, d, "c5", chunk=w["chunk"])
+
+
+@pytest.mark.parametrize("lens,D,G", [
+    ([1, 15, 16, 17, 511, 512, 513, 1000, 0, 2049], 64, 8),
+    ([3, 64, 700, 1, 0, 128], 128, 4),
+    ([129, 1030, 20], 64, 16),
+    ([5000, 77], 128, 1),
+])
+def test_edges(lib, lens, D, G):
+    Hkv = 2
+    d = W.decode_inputs(31, len(lens), Hkv * G, Hkv, D, 16, 1, max(lens), seq_lens=np.array(lens))
+    compare(lib, d, f"edges D={D} G={G}")
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 1024])
+def test_split_sizes_agree_with_oracle(lib, chunk):
+    d = W.decode_inputs(33, 6, 16, 2, 64, 16, 1, 3000)
+    compare(lib, d, "split", chunk=chunk)
+
+
+def test_split_vs_unsplit_on_gpu(lib):
+    d = W.decode_inputs(34, 8, 64, 8, 64, 16, 100, 4096)
+    o1, l1 = run(lib, d, 512, max_len=4096)
+    o2, l2 = run(lib, d, 4096, max_len=4096)
+    assert (o1.float() - o2.float()).abs().max().item() <= BF16_TOL
+    assert (l1 - l2).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("tstar", [0, 15, 16, 511, 512, "last", "rand"])
+def test_needle_is_element_exact(lib, tstar):
+    """All keys zero except logical position t*, whose key makes its score 200 above every other: every other
+    weight underflows to exactly 0 in fp32, so the output must be V[t*] bit for bit."""
+    n = 1300
+    d = W.decode_inputs(35, 2, 16, 2, 64, 16, n, n, seq_lens=np.array([n, 900]))
+    t = {"last": n - 1, "rand": 777}.get(tstar, tstar)
+    q = np.zeros_like(d.q)
+    one = W.bf16_bits_from_f32(np.float32([1.0]))[0]
+    q[0, :, 0] = one
+    kc = np.zeros_like(d.k_cache)
+    pid = d.block_table[0, t // 16]
+    big = W.bf16_bits_from_f32(np.float32([200.0 / d.scale]))[0]
+    kc[pid, :, t % 16, 0] = big
+    d2 = W.DecodeInputs(q=q, k_cache=kc, v_cache=d.v_cache, block_table=d.block_table, seq_lens=d.seq_lens,
+                        page=16, scale=d.scale)
+    o, _ = run(lib, d2)
+    want = torch.from_numpy(d.v_cache[pid, :, t % 16, :].view(np.int16)).view(torch.bfloat16)
+    got = o[0].cpu()
+    for h in range(16):
+        assert torch.equal(got[h], want[h // 8]), (tstar, h)
+
+
+def test_deterministic(lib):
+    d = W.decode_inputs(36, 4, 64, 8, 64, 16, 1000, 9000)
+    o1, l1 = run(lib, d)
+    o2, l2 = run(lib, d)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
