@@ -71,8 +71,10 @@ def test_split_vs_unsplit_on_gpu(lib):
     d = W.decode_inputs(34, 8, 64, 8, 64, 16, 100, 4096)
     o1, l1 = run(lib, d, 512, max_len=4096)
     o2, l2 = run(lib, d, 4096, max_len=4096)
+    # each split rounds its probabilities to bf16 against its own chunk max, so the two sums of rounded weights
+    # differ by up to 2^-9 relative each; lse differs by up to ~2 * 2^-9 * ln 2 plus fp32 noise
     assert (o1.float() - o2.float()).abs().max().item() <= BF16_TOL
-    assert (l1 - l2).abs().max().item() <= 1e-4
+    assert (l1 - l2).abs().max().item() <= LSE_TOL
 
 
 @pytest.mark.parametrize("tstar", [0, 15, 16, 511, 512, "last", "rand"])
