@@ -44,6 +44,8 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the 32K/128K dense and 128K sparse lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--long-reps", type=int, default=3)
+    ap.add_argument("--only", choices=["dense", "dense32k", "sparse", "decode"], default=None,
+                    help="run one path alone (for profiler runs); prints a short JSON line with its mean time")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (each GPU would run an "
@@ -62,6 +64,10 @@ def main():
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.only:
+        run_only(args, lca, W, torch, np, to_dev, dev)
+        return
 
     # ---------------------------------------------------------------------------------------- inputs
     log("generating the headline dense workload (N=4096)")
@@ -244,6 +250,49 @@ def main():
         "paths": paths,
     }
     print(json.dumps(line), flush=True)
+
+
+def run_only(args, lca, W, torch, np, to_dev, dev):
+    """One path, args.warmup + args.steps calls, for kernel-level profiler runs."""
+    if args.only in ("dense", "dense32k"):
+        name = "c2_dense_bf16_n4k" if args.only == "dense" else "c3_sparse_bf16_n32k"
+        c = W.make(name)
+        q, k, v = to_dev(c.q), to_dev(c.k), to_dev(c.v)
+        o = torch.empty_like(q)
+        fn = lambda: lca.prefill_dense(q, k, v, scale=c.scale, out=o, return_lse=False)
+    elif args.only == "sparse":
+        w = W.WORKLOADS["c3_sparse_bf16_n32k"]
+        c = W.make("c3_sparse_bf16_n32k")
+        q, k, v = to_dev(c.q), to_dev(c.k), to_dev(c.v)
+        o = torch.empty_like(q)
+        m = lca.block_mask_build(q, k, w["block"], w["keep_permille"], w["alpha"], w["q_lo_pct"], w["q_hi_pct"],
+                                 scale=c.scale, want_radius_stats=False)
+
+        def fn():
+            lca.block_mask_build(q, k, w["block"], w["keep_permille"], w["alpha"], w["q_lo_pct"], w["q_hi_pct"],
+                                 scale=c.scale, outputs=m)
+            lca.prefill_block_sparse(q, k, v, m.kv_count, m.kv_index, w["block"], scale=c.scale, out=o,
+                                     return_lse=False)
+    else:
+        w = W.WORKLOADS["c5_decode_paged_bf16"]
+        c = W.make("c5_decode_paged_bf16")
+        q, kc, vc = to_dev(c.q), to_dev(c.k_cache), to_dev(c.v_cache)
+        bt, sl = torch.from_numpy(c.block_table).to(dev), torch.from_numpy(c.seq_lens).to(dev)
+        o = torch.empty_like(q)
+        ws = torch.empty(lca.decode_workspace_bytes(q, kc, bt, w["len_hi"], w["chunk"]), dtype=torch.uint8, device=dev)
+        fn = lambda: lca.decode_paged(q, kc, vc, bt, sl, w["len_hi"], w["chunk"], scale=c.scale, out=o,
+                                      return_lse=False, workspace=ws)
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"only": args.only, "calls": args.steps, "ms_per_call": a.elapsed_time(b) / args.steps}),
+          flush=True)
 
 
 if __name__ == "__main__":

@@ -29,79 +29,55 @@ namespace {
 constexpr int kBN = 64;        // keys per KV tile
 constexpr float kSlack = 8.0f; // lazy-rescale threshold, log2 units
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// K and V tiles (64 keys x D, bf16) live in LDS in their natural row-major layout without padding; 16-byte chunk c
+// of row r sits at chunk position c ^ swz(r). The swizzle keeps both access patterns free of bank conflicts:
+// the 16-byte K reads of 16 consecutive rows, and the 8-byte transposed V reads of four consecutive keys.
 template <int D>
 struct Lds {
-    static constexpr int KP = D * 2 + 16;   // K row pitch in bytes (padding spreads rows over the banks)
-    static constexpr int VP = kBN * 2 + 16; // V^T row pitch in bytes
-    static constexpr int KBYTES = kBN * KP;
-    static constexpr int VBYTES = D * VP;
-    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int ROWB = D * 2;            // bytes per key row
+    static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+    static constexpr int TILE = kBN * ROWB;       // one K or V tile
+    static constexpr int LOADS = TILE / 1024;     // 64-lane x 16-byte direct loads per tile
+    __device__ static __forceinline__ int swz(int r) {
+        return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+    }
 };
 
-// Column of key k (0..63) inside a V^T row: bits 2 and 3 of the key's index within its 16-key group are swapped,
-// so the eight keys one MFMA lane group contracts over sit next to each other.
-__device__ __forceinline__ int vt_pos(int k) {
-    const int w = k & 15;
-    return (k & ~15) | ((w & 4) << 1) | ((w & 8) >> 1) | (w & 3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, bytes, 0x00020000);
 }
 
-template <int D, int NT>
-struct Stager {
-    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-    static constexpr int KCH = kBN * CPR;              // K chunks per tile
-    static constexpr int KPT = (KCH + NT - 1) / NT;
-    static constexpr int VU = (kBN / 2) * CPR;         // (key pair, chunk) units per tile
-    static constexpr int VPT = (VU + NT - 1) / NT;
-    u32x4 kr[KPT];
-    u32x4 vr[VPT][2];
-
-    __device__ __forceinline__ void load(const uint16_t* kb, const uint16_t* vb, int kv0, int N, int tid) {
+// Direct global->LDS staging of one tile by the work-group's NW waves: each 64-lane load moves 1 KiB into
+// consecutive LDS bytes, lane l's 16 bytes to position l; the lane fetches the global chunk that the swizzle puts
+// there. Buffer range checking returns zeros for keys outside [0, N) (including negative tile starts).
+template <int D, int NW>
+struct TileLoader {
+    static constexpr int PER = (Lds<D>::LOADS + NW - 1) / NW;
+    int voff[PER];
+    int first;   // this wave's first load slot
+    __device__ __forceinline__ void init(int w, int lane) {
+        first = w * PER;
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int idx = tid + i * NT;
-            kr[i] = u32x4{0u, 0u, 0u, 0u};
-            if (KCH % NT == 0 || idx < KCH) {
-                const int key = kv0 + idx / CPR;
-                if ((unsigned)key < (unsigned)N) kr[i] = load16(kb + (size_t)key * D + (idx % CPR) * 8);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int idx = tid + i * NT;
-            vr[i][0] = u32x4{0u, 0u, 0u, 0u};
-            vr[i][1] = u32x4{0u, 0u, 0u, 0u};
-            if (VU % NT == 0 || idx < VU) {
-                const int key = kv0 + 2 * (idx / CPR);
-                const int c = idx % CPR;
-                if ((unsigned)key < (unsigned)N) vr[i][0] = load16(vb + (size_t)key * D + c * 8);
-                if ((unsigned)(key + 1) < (unsigned)N) vr[i][1] = load16(vb + (size_t)(key + 1) * D + c * 8);
-            }
+        for (int i = 0; i < PER; ++i) {
+            const int z = (first + i) * 64 + lane;           // 16-byte slot inside the tile
+            const int r = z / Lds<D>::CPR, pc = z % Lds<D>::CPR;
+            voff[i] = r * Lds<D>::ROWB + ((pc ^ Lds<D>::swz(r)) * 16);
         }
     }
-
-    __device__ __forceinline__ void store(char* lds, int tid) const {
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int kv0) const {
+        const int soff = kv0 * Lds<D>::ROWB;
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int idx = tid + i * NT;
-            if (KCH % NT == 0 || idx < KCH) store16(lds + (idx / CPR) * Lds<D>::KP + (idx % CPR) * 16, kr[i]);
-        }
-        char* vt = lds + Lds<D>::KBYTES;
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int idx = tid + i * NT;
-            if (VU % NT == 0 || idx < VU) {
-                const int p = idx / CPR, c = idx % CPR;
-                const int col = vt_pos(2 * p) * 2;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t a = vr[i][0][e >> 1], b = vr[i][1][e >> 1];
-                    const uint32_t w = (e & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-                    *reinterpret_cast<uint32_t*>(vt + (c * 8 + e) * Lds<D>::VP + col) = w;
-                }
-            }
-        }
+        for (int i = 0; i < PER; ++i)
+            if (Lds<D>::LOADS % NW == 0 || first + i < Lds<D>::LOADS)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + (first + i) * 1024),
+                                                         16, voff[i], soff, 0, 0);
     }
 };
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 template <int D>
 struct RowState {
@@ -110,22 +86,40 @@ struct RowState {
     float l;  // this lane's share of the row sum
 };
 
-// One KV tile for one wave. `lds` points at a staged tile (K rows, then V^T rows).
+// S^T for a 64-key tile: two 32x32 blocks (keys x this wave's 32 query rows); the two accumulators alternate.
 template <int D>
-__device__ __forceinline__ void tile_step(const char* lds, const bf16x8 (&qf)[D / 16], RowState<D>& st, float c2,
-                                          bool diag, int kv0, int qrow, int lane) {
+__device__ __forceinline__ void qk_tile(const lds_char* kl, const bf16x8 (&qf)[D / 16], f32x16 (&s)[2], int lane) {
     const int hi = lane >> 5, ln = lane & 31;
-    f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        s[t] = f32x16{};
+    for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8*>(lds + (32 * t + ln) * Lds<D>::KP + (16 * ks + 8 * hi) * 2);
-            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[t], 0, 0, 0);
+        for (int t = 0; t < 2; ++t) {
+            const int r = 32 * t + ln;
+            const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                kl + r * Lds<D>::ROWB + (((2 * ks + hi) ^ Lds<D>::swz(r)) * 16));
+            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
         }
-    }
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+    // lanes l and l^32 hold the two halves of one query row's keys
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Online-softmax update for one tile: row max (lazy refresh), probabilities rounded to bf16 and packed in the
+// B-operand order of the PV product, row-sum share updated with the rounded values.
+template <int D>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], uint32_t (&pw)[2][8], RowState<D>& st, float c2,
+                                             bool diag, int kv0, int qrow, int lane) {
+    const int hi = lane >> 5;
     if (diag) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -135,25 +129,26 @@ __device__ __forceinline__ void tile_step(const char* lds, const bf16x8 (&qf)[D 
                 if (key > qrow) s[t][r] = -INFINITY;
             }
     }
-    float mx = s[0][0];
+    float c[4];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    for (int k = 0; k < 4; ++k) c[k] = fmaxf(fmaxf(s[0][k], s[0][k + 4]), fmaxf(s[0][k + 8], s[0][k + 12]));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int k = 0; k < 4; ++k)
+        c[k] = fmaxf(c[k], fmaxf(fmaxf(s[1][k], s[1][k + 4]), fmaxf(s[1][k + 8], s[1][k + 12])));
+    const float mx = pair_max(fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])));
     const float mxs = mx * c2;
     if (mxs > st.m + kSlack) {
-        const float alpha = exp2f(st.m - mxs);
+        const float alpha = __builtin_amdgcn_exp2f(st.m - mxs);
         st.l *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) st.o[dt] *= alpha;
         st.m = mxs;
     }
     const float bias = (st.m == -INFINITY) ? 0.0f : -st.m;
-    uint32_t pw[2][8];
     bf16x2 ones;
     ones[0] = (__bf16)1.0f;
     ones[1] = (__bf16)1.0f;
+    float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -161,21 +156,52 @@ __device__ __forceinline__ void tile_step(const char* lds, const bf16x8 (&qf)[D 
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * w], c2, bias));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * w + 1], c2, bias));
             pw[t][w] = pack_bf16x2(p0, p1);
-            st.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[t][w]), ones, st.l, false);
+            if (w & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[t][w]), ones, l1, false);
+            else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[t][w]), ones, l0, false);
         }
-    const char* vt = lds + Lds<D>::KBYTES;
+    st.l += l0 + l1;
+}
+
+// Per-lane byte offsets of the transposed V reads. The A operand of a PV MFMA holds, in lane (ln, hi), the head
+// dim d = 32*dt + ln for the eight keys of slots 8*hi .. 8*hi+7; two ds_read_b64_tr_b16 produce them, each
+// giving a 16-lane group 16 consecutive d for 4 consecutive keys: source lane 4*jj + a of the group points at
+// V[key_jj][d0 + 4a], and output lane i receives V[key_0..3][d0 + i].
+template <int D>
+struct VtAddr {
+    int key_lo;  // this lane's source key inside a 16-key slice: 4*hi + jj (the second read adds 8)
+    int dq;      // this lane's source head-dim offset inside a 32-wide tile: 16*half + 4*a
+    __device__ __forceinline__ void init(int lane) {
+        key_lo = 4 * (lane >> 5) + ((lane & 15) >> 2);
+        dq = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    }
+    __device__ __forceinline__ int at(int key, int d) const {
+        return key * Lds<D>::ROWB + (((d >> 3) ^ Lds<D>::swz(key)) * 16) + (d & 7) * 2;
+    }
+};
+
+// O^T += V^T P^T over the tile's 64 keys.
+template <int D>
+__device__ __forceinline__ void pv_tile(const lds_char* vl, const VtAddr<D>& va, const uint32_t (&pw)[2][8],
+                                        RowState<D>& st) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8 b = __builtin_bit_cast(
+                bf16x8, (u32x4{pw[t][4 * u], pw[t][4 * u + 1], pw[t][4 * u + 2], pw[t][4 * u + 3]}));
+            const int key = 32 * t + 16 * u + va.key_lo;
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * dt + ln) * Lds<D>::VP +
-                                                                  (32 * t + 16 * u + 8 * hi) * 2);
-                const bf16x8 b = __builtin_bit_cast(
-                    bf16x8, (u32x4{pw[t][4 * u], pw[t][4 * u + 1], pw[t][4 * u + 2], pw[t][4 * u + 3]}));
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const int d = 32 * dt + va.dq;
+                typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + va.at(key, d)));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + va.at(key + 8, d)));
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, (u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                                   __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]}));
                 st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, st.o[dt], 0, 0, 0);
             }
+        }
 }
 
 template <int D>
@@ -191,7 +217,7 @@ template <int D>
 __device__ __forceinline__ void finish_rows(const RowState<D>& st, uint16_t* oh, float* lse_row, int qrow, int N,
                                             int lane) {
     const int hi = lane >> 5;
-    const float lt = st.l + __shfl_xor(st.l, 32);
+    const float lt = pair_sum(st.l);
     if (qrow >= N) return;
     const float inv = 1.0f / lt;
 #pragma unroll
@@ -215,6 +241,81 @@ __device__ __forceinline__ void init_state(RowState<D>& st) {
     st.l = 0.0f;
 }
 
+// LDS of one work-group: two K and two V tiles.
+template <int D>
+struct Tiles {
+    lds_char* k[2];
+    lds_char* v[2];
+};
+
+// The KV loop of one work-group, software-pipelined inside every wave: while the VALU turns tile j's scores
+// into probabilities, the matrix cores already compute tile j+1's scores; then tile j's PV product. K is staged
+// one tile ahead of V so both are resident: during step j LDS holds K(j+1) and V(j), and the step's loads of
+// K(j+2) and V(j+1) stream straight into the buffers step j-1 finished with. One barrier per step; the
+// buffer parity is a compile-time constant inside each unrolled step.
+// kv_of(t) gives tile t's first key; a wave skips tiles that start past its last row, and masks elements only on
+// tiles that reach past its first row.
+template <int D, int NW, int PAR, typename KvOf>
+__device__ __forceinline__ void attend_step(const Tiles<D>& tl, const TileLoader<D, NW>& ld,
+                                            __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, const VtAddr<D>& va,
+                                            int j, int ntiles, KvOf kv_of, int& kv_cur, int& kv_nxt,
+                                            const bf16x8 (&qf)[D / 16], f32x16 (&scur)[2], f32x16 (&snext)[2],
+                                            RowState<D>& st, float c2, int q0, int wave_last, int lane) {
+    const int qrow = q0 + (lane & 31);
+    const bool has_next = j + 1 < ntiles;
+    const bool act = kv_cur <= wave_last;
+    const bool act_n = has_next && kv_nxt <= wave_last;
+    const bool diag = kv_cur + kBN - 1 > q0;
+    const int kv_2 = j + 2 < ntiles ? kv_of(j + 2) : 0;
+    if (j + 2 < ntiles) ld.load(krs, tl.k[PAR], kv_2);
+    if (has_next) ld.load(vrs, tl.v[1 - PAR], kv_nxt);
+    uint32_t pw[2][8];
+    if (act && act_n && !diag) {
+        // steady state: one basic block so the scheduler can interleave the two MFMA streams with the VALU
+        softmax_tile<D>(scur, pw, st, c2, false, kv_cur, qrow, lane);
+        qk_tile<D>(tl.k[1 - PAR], qf, snext, lane);
+        pv_tile<D>(tl.v[PAR], va, pw, st);
+    } else {
+        if (act) softmax_tile<D>(scur, pw, st, c2, diag, kv_cur, qrow, lane);
+        if (act_n) qk_tile<D>(tl.k[1 - PAR], qf, snext, lane);
+        if (act) pv_tile<D>(tl.v[PAR], va, pw, st);
+    }
+    wait_vmem();
+    __syncthreads();
+    kv_cur = kv_nxt;
+    kv_nxt = kv_2;
+}
+
+template <int D, int NW, typename KvOf>
+__device__ __forceinline__ void attend(const Tiles<D>& tl, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                       int ntiles, KvOf kv_of, const bf16x8 (&qf)[D / 16], RowState<D>& st, float c2,
+                                       int q0, int wave_last, int w, int lane) {
+    TileLoader<D, NW> ld;
+    ld.init(w, lane);
+    VtAddr<D> va;
+    va.init(lane);
+    int kv_cur = kv_of(0);
+    int kv_nxt = ntiles > 1 ? kv_of(1) : 0;
+    ld.load(krs, tl.k[0], kv_cur);
+    ld.load(vrs, tl.v[0], kv_cur);
+    if (ntiles > 1) ld.load(krs, tl.k[1], kv_nxt);
+    wait_vmem();
+    __syncthreads();
+    f32x16 sa[2], sb[2];
+    if (kv_cur <= wave_last) qk_tile<D>(tl.k[0], qf, sa, lane);
+    __syncthreads();
+    int j = 0;
+    for (; j + 1 < ntiles; j += 2) {
+        attend_step<D, NW, 0>(tl, ld, krs, vrs, va, j, ntiles, kv_of, kv_cur, kv_nxt, qf, sa, sb, st, c2, q0,
+                              wave_last, lane);
+        attend_step<D, NW, 1>(tl, ld, krs, vrs, va, j + 1, ntiles, kv_of, kv_cur, kv_nxt, qf, sb, sa, st, c2, q0,
+                              wave_last, lane);
+    }
+    if (j < ntiles)
+        attend_step<D, NW, 0>(tl, ld, krs, vrs, va, j, ntiles, kv_of, kv_cur, kv_nxt, qf, sa, sb, st, c2, q0,
+                              wave_last, lane);
+}
+
 struct DenseArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -234,7 +335,11 @@ struct DenseArgs {
 // head cycles fastest so that, with 8 XCDs dispatched round-robin, an XCD keeps seeing the same kv heads.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void prefill_dense_bf16_kernel(const DenseArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[2 * Lds<D>::STAGE];
+    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::TILE];
+    __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::TILE];
+    __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::TILE];
+    __shared__ __attribute__((aligned(1024))) char v1[Lds<D>::TILE];
+    const Tiles<D> tl{{(lds_char*)k0, (lds_char*)k1}, {(lds_char*)v0, (lds_char*)v1}};
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int per_tile = a.B * a.Hkv * a.NHG;
     const int pt = a.n_ptiles - 1 - (int)(blockIdx.x / per_tile);
@@ -248,31 +353,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_dense_bf16_kernel(const Dense
     const int q0 = p0 + 32 * (w / a.HPW);
     const int wg_end = min(a.N, p0 + a.PPW);
     const int ntiles = (wg_end + kBN - 1) / kBN;
-    const int ln = lane & 31;
-    const int qrow = q0 + ln;
+    const int qrow = q0 + (lane & 31);
 
     const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)a.N * D;
-    const uint16_t* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.N * D;
-    const uint16_t* vb = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.N * D;
+    const size_t kvoff = ((size_t)b * a.Hkv + g) * (size_t)a.N * D;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + kvoff, a.N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v + kvoff, a.N * D * 2);
 
     bf16x8 qf[D / 16];
     load_q<D>(qf, a.q + qoff, qrow, a.N, lane);
     RowState<D> st;
     init_state<D>(st);
-
-    Stager<D, NW * 64> sg;
-    sg.load(kb, vb, 0, a.N, tid);
-    sg.store(lds, tid);
-    __syncthreads();
-    const int wave_last = min(q0 + 31, a.N - 1);
-    for (int j = 0; j < ntiles; ++j) {
-        if (j + 1 < ntiles) sg.load(kb, vb, (j + 1) * kBN, a.N, tid);
-        const int kv0 = j * kBN;
-        if (q0 < a.N && kv0 <= wave_last)
-            tile_step<D>(lds + (j & 1) * Lds<D>::STAGE, qf, st, a.c2, kv0 + kBN - 1 > q0, kv0, qrow, lane);
-        if (j + 1 < ntiles) sg.store(lds + ((j + 1) & 1) * Lds<D>::STAGE, tid);
-        __syncthreads();
-    }
+    const int wave_last = q0 < a.N ? min(q0 + 31, a.N - 1) : -1;
+    attend<D, NW>(tl, krs, vrs, ntiles, [](int t) { return t * kBN; }, qf, st, a.c2, q0, wave_last, w, lane);
     finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
 }
 
@@ -293,7 +386,11 @@ struct SparseArgs {
 // are never read. Rows are issued latest block first, as they tend to hold the longest lists.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void prefill_sparse_bf16_kernel(const SparseArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[2 * Lds<D>::STAGE];
+    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::TILE];
+    __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::TILE];
+    __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::TILE];
+    __shared__ __attribute__((aligned(1024))) char v1[Lds<D>::TILE];
+    const Tiles<D> tl{{(lds_char*)k0, (lds_char*)k1}, {(lds_char*)v0, (lds_char*)v1}};
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int per = a.B * a.Hq;
     const int i = a.nb - 1 - (int)(blockIdx.x / per);
@@ -310,34 +407,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_sparse_bf16_kernel(const Spar
     const int ntiles = cnt * sub;
 
     const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)a.N * D;
-    const uint16_t* kb = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.N * D;
-    const uint16_t* vb = a.v + ((size_t)b * a.Hkv + g) * (size_t)a.N * D;
+    const size_t kvoff = ((size_t)b * a.Hkv + g) * (size_t)a.N * D;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + kvoff, a.N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v + kvoff, a.N * D * 2);
 
     bf16x8 qf[D / 16];
     load_q<D>(qf, a.q + qoff, qrow, a.N, lane);
     RowState<D> st;
     init_state<D>(st);
     if (ntiles == 0) return;  // every valid list holds the diagonal; an empty one leaves the rows unwritten
-
-    Stager<D, NW * 64> sg;
-    int jb = list[0];
-    sg.load(kb, vb, jb * a.block, a.N, tid);
-    sg.store(lds, tid);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int kv0 = jb * a.block + (t % sub) * kBN;
-        const bool diag = (jb == i);
-        if (t + 1 < ntiles) {
-            const int jn = list[(t + 1) / sub];
-            sg.load(kb, vb, jn * a.block + ((t + 1) % sub) * kBN, a.N, tid);
-            if ((t + 1) % sub == 0) jb = jn;
-        }
-        if (kv0 <= q0 + 31)
-            tile_step<D>(lds + (t & 1) * Lds<D>::STAGE, qf, st, a.c2, diag && (kv0 + kBN - 1 > q0), kv0, qrow,
-                         lane);
-        if (t + 1 < ntiles) sg.store(lds + ((t + 1) & 1) * Lds<D>::STAGE, tid);
-        __syncthreads();
-    }
+    const int blk = a.block;
+    attend<D, NW>(tl, krs, vrs, ntiles, [=](int t) { return list[t / sub] * blk + (t % sub) * kBN; }, qf, st, a.c2,
+                  q0, q0 + 31, w, lane);
     finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
 }
 
