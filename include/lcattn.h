@@ -148,7 +148,7 @@ size_t attn_decode_workspace_bytes(const attn_decode_shape_t* shape, int32_t max
  *   o         bf16 [batch, heads_q, head_dim]; lse optional fp32 [batch, heads_q] (NULL to skip).
  * Cache slots at or past seq_lens[b] and pages the table does not reference may hold any bits, NaN included;
  * they never reach the output. seq_lens[b] == 0 gives o = 0 and lse = -inf.
- * Supported: head_dim 64 or 128, page_size 16, chunk_tokens a multiple of 64, heads_q / heads_kv <= 16.
+ * Supported: head_dim 64 or 128, page_size 16, chunk_tokens a multiple of 64 up to 4096, heads_q / heads_kv <= 16.
  */
 attn_status_t attn_decode_paged(const attn_decode_shape_t* shape, const void* q, const void* k_cache,
                                 const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,

@@ -100,7 +100,8 @@ attn_status_t check_decode_shape(const attn_decode_shape_t* s, int32_t max_seq_l
     if (s->heads_q / s->heads_kv > 16) return fail(ATTN_ERR_UNSUPPORTED, "more than 16 query heads per kv head");
     if (s->head_dim != 64 && s->head_dim != 128) return fail(ATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     if (s->page_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "page_size must be 16");
-    if (s->chunk_tokens < 64 || s->chunk_tokens % 64) return fail(ATTN_ERR_UNSUPPORTED, "chunk_tokens must be a multiple of 64");
+    if (s->chunk_tokens < 64 || s->chunk_tokens % 64 || s->chunk_tokens > 4096)
+        return fail(ATTN_ERR_UNSUPPORTED, "chunk_tokens must be a multiple of 64 in [64, 4096]");
     if (!(std::isfinite(s->scale) && s->scale > 0.0f)) return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
     if (max_seq_len < 0) return fail(ATTN_ERR_SHAPE, "max_seq_len must be >= 0");
     if ((long long)max_seq_len > (long long)s->max_pages_per_seq * s->page_size)

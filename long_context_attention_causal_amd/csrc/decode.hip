@@ -21,7 +21,10 @@ namespace lcattn {
 namespace {
 
 constexpr int kPage = 16;
-constexpr int kVtPitch = kPage * 2 + 8;   // bytes per V^T row inside one page's slab in LDS
+constexpr int kPB = 2;   // pages per batch; each wave double-buffers two batches
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
 
 struct SplitArgs {
     const uint16_t* q;
@@ -35,22 +38,42 @@ struct SplitArgs {
     float c2;
 };
 
-// PB pages per batch and wave; the wave walks its ppw pages in batches.
-template <int D, int PB>
+// A buffer view of one (page, kv head) slab of 16 x D bf16 whose size stops at the sequence end: slots past it, and
+// whole pages past it or outside the pool, read as zeros, so cache padding (NaN included) never reaches the maths.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const uint16_t* cache, int pid, int hkv, int g, int valid,
+                                                            int D) {
+    const uint16_t* base = cache + ((size_t)pid * hkv + g) * (size_t)kPage * D;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, valid * D * 2, 0x00020000);
+}
+
+template <int D>
+struct Batch {
+    u32x4 k[kPB][D / 32];   // K slabs straight into the MFMA A-operand layout
+    int tok0;               // first logical token of the batch
+};
+
+// Work-group = (chunk of chunk_tokens tokens, kv head, sequence); 4 waves, each streaming its ppw pages in
+// batches of kPB pages with the next batch in flight while the current one is used. K goes to VGPRs in the A
+// layout of v_mfma_f32_16x16x32_bf16 (lane = token row, 16-byte pieces of the head dim) and S^T = K Q^T has the
+// kv group's query heads as columns. V goes straight to LDS in its natural layout and comes back as the A
+// operand of v_mfma_f32_16x16x16_bf16 through ds_read_b64_tr_b16 (a 16-lane group receives 16 head-dim rows x 4
+// tokens); the bf16 probabilities are the B operand in the lane that computed them.
+template <int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(const SplitArgs a) {
-    constexpr int KS = D / 32;                  // K operand pieces per page (16x16x32 MFMAs per page)
-    constexpr int VL = (kPage * D) / (64 * 8);  // 16-byte V loads per lane per page
-    constexpr int DT = D / 16;                  // 16-row tiles of the head dim
-    __shared__ __attribute__((aligned(16))) char vt_all[4 * PB * D * kVtPitch];
+    constexpr int KS = D / 32;                    // 16x16x32 MFMAs per page for S^T
+    constexpr int DT = D / 16;                    // 16-row tiles of the head dim for O^T
+    constexpr int SLAB = kPage * D * 2;           // bytes per page slab
+    constexpr int VLOADS = SLAB / 1024;           // 1 KiB direct loads per slab
+    __shared__ __attribute__((aligned(1024))) char vbuf[4][2][kPB * SLAB];   // [wave][buffer]
     __shared__ float red_m[4][16];
     __shared__ float red_l[4][16];
 
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int L = a.lens[b];
     if (c * a.chunk >= L) return;  // uniform over the work-group
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, so page lookups stay scalar
     const int n = lane & 15, grp = lane >> 4;
-    char* vt = vt_all + w * PB * D * kVtPitch;
 
     bf16x8 qf[KS];
 #pragma unroll
@@ -62,48 +85,69 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const SplitArgs a) {
     const int npages_seq = (L + kPage - 1) / kPage;
     const int wpage0 = c * (a.chunk / kPage) + w * a.ppw;
     const int32_t* btrow = a.bt + (size_t)b * a.max_pages;
-    const size_t slab = (size_t)kPage * D;
+    const int nbatch = (a.ppw + kPB - 1) / kPB;
+    // the wave's block-table entries in one load (lane i <-> page wpage0 + i; ppw <= 64), read out with readlane
+    const int my_page = wpage0 + lane;
+    const int my_pid = (lane < a.ppw && my_page < npages_seq && my_page < a.max_pages) ? btrow[my_page] : 0;
+
+    // issue batch `bi` into buffer `buf`
+    auto issue = [&](int bi, int buf, Batch<D>& bt) {
+        bt.tok0 = (wpage0 + bi * kPB) * kPage;
+#pragma unroll
+        for (int p = 0; p < kPB; ++p) {
+            const int lp = wpage0 + bi * kPB + p;
+            const bool inrange = bi * kPB + p < a.ppw && lp < npages_seq && lp < a.max_pages;
+            int pid = inrange ? __builtin_amdgcn_readlane(my_pid, bi * kPB + p) : 0;
+            int valid = inrange ? min(kPage, L - lp * kPage) : 0;
+            if ((unsigned)pid >= (unsigned)a.num_pages) {
+                pid = 0;
+                valid = 0;
+            }
+            const __amdgpu_buffer_rsrc_t kr = slab_rsrc(a.kc, pid, a.Hkv, g, valid, D);
+            const __amdgpu_buffer_rsrc_t vr = slab_rsrc(a.vc, pid, a.Hkv, g, valid, D);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                bt.k[p][ks] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, (n * D + 32 * ks + 8 * grp) * 2, 0, 0));
+            lds_char* dst = (lds_char*)&vbuf[w][buf][p * SLAB];
+#pragma unroll
+            for (int i = 0; i < VLOADS; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(dst + i * 1024),
+                                                         16, (i * 64 + lane) * 16, 0, 0, 0);
+        }
+    };
 
     f32x4 o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{};
     float m = -INFINITY, l = 0.0f;
+    bf16x2 ones;
+    ones[0] = (__bf16)1.0f;
+    ones[1] = (__bf16)1.0f;
 
-    for (int pb0 = 0; pb0 < a.ppw; pb0 += PB) {
-        u32x4 kr[PB][KS], vr[PB][VL];
-        bool pv[PB];
-#pragma unroll
-        for (int p = 0; p < PB; ++p) {
-            const int lp = wpage0 + pb0 + p;
-            pv[p] = (pb0 + p < a.ppw) && lp < npages_seq && lp < a.max_pages;
-            const uint16_t* ks_ = nullptr;
-            const uint16_t* vs_ = nullptr;
-            if (pv[p]) {
-                const int pid = btrow[lp];
-                pv[p] = (unsigned)pid < (unsigned)a.num_pages;   // out-of-pool entries read as masked slots
-                ks_ = a.kc + ((size_t)pid * a.Hkv + g) * slab;
-                vs_ = a.vc + ((size_t)pid * a.Hkv + g) * slab;
-            }
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kr[p][ks] = pv[p] ? load16(ks_ + n * D + 32 * ks + 8 * grp) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int i = 0; i < VL; ++i) vr[p][i] = pv[p] ? load16(vs_ + (i * 64 + lane) * 8) : u32x4{0u, 0u, 0u, 0u};
+    // one batch: issue the next batch into the other register set and LDS buffer, wait for this one, use it
+    auto run = [&](int bi, int buf, Batch<D>& cur, Batch<D>& nxt) {
+        if (bi + 1 < nbatch) {
+            issue(bi + 1, buf ^ 1, nxt);
+            __builtin_amdgcn_s_waitcnt(0x0F70 | ((KS + VLOADS) * kPB & 15) | ((((KS + VLOADS) * kPB) >> 4) << 14));
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         }
-        // scores: S^T[token = 4*grp + r][head n] per page
-        f32x4 s[PB];
+        // scores S^T[token = 4*grp + r][head n] per page
+        f32x4 s[kPB];
         float mx = -INFINITY;
 #pragma unroll
-        for (int p = 0; p < PB; ++p) {
+        for (int p = 0; p < kPB; ++p) {
             s[p] = f32x4{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                s[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[p][ks]), qf[ks], s[p], 0,
-                                                               0, 0);
-            const int tok0 = (wpage0 + pb0 + p) * kPage + 4 * grp;
+                s[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[p][ks]), qf[ks], s[p],
+                                                               0, 0, 0);
+            const int tok = cur.tok0 + p * kPage + 4 * grp;
+            const bool page_in_wave = bi * kPB + p < a.ppw;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                if (!pv[p] || tok0 + r >= L) s[p][r] = -INFINITY;
+                if (tok + r >= L || !page_in_wave) s[p][r] = -INFINITY;
                 mx = fmaxf(mx, s[p][r]);
             }
         }
@@ -111,61 +155,55 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const SplitArgs a) {
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mxs = mx * a.c2;
         if (mxs > m) {
-            const float alpha = exp2f(m - mxs);
+            const float alpha = __builtin_amdgcn_exp2f(m - mxs);
             l *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
             m = mxs;
         }
         const float bias = (m == -INFINITY) ? 0.0f : -m;
-        // V^T into LDS: slab row t, 8 head-dim values per 16-byte load
-        __syncthreads();
+        // the V slabs of this batch must be visible to every lane of the wave before the transposed reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int p = 0; p < PB; ++p) {
-            char* vp = vt + p * D * kVtPitch;
-#pragma unroll
-            for (int i = 0; i < VL; ++i) {
-                const int e0 = (i * 64 + lane) * 8;
-                const int t = e0 / D, d0 = e0 % D;
-                const bool ok = pv[p] && (wpage0 + pb0 + p) * kPage + t < L;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t word = vr[p][i][e >> 1];
-                    const uint16_t hv = ok ? (uint16_t)((e & 1) ? (word >> 16) : (word & 0xFFFFu)) : (uint16_t)0;
-                    *reinterpret_cast<uint16_t*>(vp + (d0 + e) * kVtPitch + t * 2) = hv;
-                }
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int p = 0; p < PB; ++p) {
-            float p4[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p4[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[p][r], a.c2, bias));
-            }
-            const uint32_t w0 = pack_bf16x2(p4[0], p4[1]), w1 = pack_bf16x2(p4[2], p4[3]);
+        for (int p = 0; p < kPB; ++p) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[p][0], a.c2, bias));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[p][1], a.c2, bias));
+            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[p][2], a.c2, bias));
+            const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[p][3], a.c2, bias));
+            const uint32_t w0 = pack_bf16x2(p0, p1), w1 = pack_bf16x2(p2, p3);
             const bf16x4 pb = __builtin_bit_cast(bf16x4, (u32x2{w0, w1}));
-            bf16x2 ones;
-            ones[0] = (__bf16)1.0f;
-            ones[1] = (__bf16)1.0f;
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, l, false);
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, l, false);
-            const char* vp = vt + p * D * kVtPitch;
+            // source lane 4*jj + aa of 16-lane group grp points at V[token 4*grp + jj][16*dt + 4*aa]
+            const lds_char* slab = (const lds_char*)&vbuf[w][buf][p * SLAB];
+            const int src = (4 * grp + ((lane & 15) >> 2)) * D * 2 + 8 * (lane & 3);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const bf16x4 av =
-                    __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(vp + (16 * dt + n) * kVtPitch + 8 * grp));
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, o[dt], 0, 0, 0);
+                typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+                const v4i16 av = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(slab + src + 32 * dt));
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, av), pb, o[dt], 0, 0, 0);
             }
         }
+        // all lanes are done reading this buffer before the next batch's loads may target it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    Batch<D> ba, bb;
+    issue(0, 0, ba);
+    for (int bi = 0; bi < nbatch; bi += 2) {
+        run(bi, 0, ba, bb);
+        if (bi + 1 < nbatch) run(bi + 1, 1, bb, ba);
     }
     // wave partial -> LDS: this lane holds O^T[d = 16*dt + 4*grp + r][head n], sum share l, max m (same over a
     // head's lanes)
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    __syncthreads();  // all waves are done with their V^T slabs; reuse the space for the merge
-    float* red_o = reinterpret_cast<float*>(vt_all);  // [4 waves][16 heads][D]
+    __syncthreads();  // every wave is done with its V buffers; reuse the space for the merge
+    float* red_o = reinterpret_cast<float*>(&vbuf[0][0][0]);  // [4 waves][16 heads][D]
     if (grp == 0) {
         red_m[w][n] = m;
         red_l[w][n] = l;
@@ -175,7 +213,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const SplitArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) red_o[(w * 16 + n) * D + 16 * dt + 4 * grp + r] = o[dt][r];
     __syncthreads();
-    // merge: thread -> (head, d) pairs
     for (int e = tid; e < a.G * D; e += 256) {
         const int hn = e / D, d = e % D;
         float M = red_m[0][hn];
@@ -185,7 +222,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const SplitArgs a) {
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
             const float mw = red_m[ww][hn];
-            const float sc = mw == -INFINITY ? 0.0f : exp2f(mw - M);
+            const float sc = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
             acc += sc * red_o[(ww * 16 + hn) * D + d];
             lsum += sc * red_l[ww][hn];
         }
@@ -220,19 +257,39 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const CombineArgs a
         if (a.lse && lane == 0) a.lse[bh] = -INFINITY;
         return;
     }
+    // chunk weights: lane c holds chunk c (and c + 64, ...)
     float M = -INFINITY;
-    for (int c = lane; c < nc; c += 64) M = fmaxf(M, lp[c]);
+    for (int c0 = 0; c0 < nc; c0 += 64) M = fmaxf(M, c0 + lane < nc ? lp[c0 + lane] : -INFINITY);
     M = wave_max(M);
     float acc[D / 64];
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) acc[k] = 0.0f;
     float sw = 0.0f;
-    for (int c = 0; c < nc; ++c) {
-        const float wc = expf(lp[c] - M);
-        sw += wc;
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+        const float wl = c0 + lane < nc ? expf(lp[c0 + lane] - M) : 0.0f;
+        sw += wl;
+        const int cn = min(64, nc - c0);
+        int c = 0;
+        for (; c + 8 <= cn; c += 8) {
+            float v[8][D / 64];
 #pragma unroll
-        for (int k = 0; k < D / 64; ++k) acc[k] = __builtin_fmaf(wc, op[(size_t)c * D + lane + 64 * k], acc[k]);
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int k = 0; k < D / 64; ++k) v[u][k] = op[(size_t)(c0 + c + u) * D + lane + 64 * k];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float wc = __shfl(wl, c + u);
+#pragma unroll
+                for (int k = 0; k < D / 64; ++k) acc[k] = __builtin_fmaf(wc, v[u][k], acc[k]);
+            }
+        }
+        for (; c < cn; ++c) {
+            const float wc = __shfl(wl, c);
+#pragma unroll
+            for (int k = 0; k < D / 64; ++k) acc[k] = __builtin_fmaf(wc, op[(size_t)(c0 + c) * D + lane + 64 * k], acc[k]);
+        }
     }
+    sw = wave_sum(sw);
     const float inv = 1.0f / sw;
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) orow[lane + 64 * k] = __builtin_bit_cast(uint16_t, (__bf16)(acc[k] * inv));
@@ -271,8 +328,8 @@ hipError_t launch_decode_paged(const DecodeProblem& p, void* workspace, hipStrea
     a.c2 = p.scale * kLog2e;
     if (C > 0) {
         const dim3 grid((unsigned)C, (unsigned)p.Hkv, (unsigned)p.B);
-        if (p.D == 64) hipLaunchKernelGGL((decode_split_kernel<64, 8>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((decode_split_kernel<128, 4>), grid, dim3(256), 0, s, a);
+        if (p.D == 64) hipLaunchKernelGGL((decode_split_kernel<64>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((decode_split_kernel<128>), grid, dim3(256), 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
