@@ -32,6 +32,22 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(key, source):
+    """HBM bytes per launch recorded in profiles/traffic.txt from rocprofv3 FETCH_SIZE/WRITE_SIZE runs (scaled by a
+    plain-copy calibration), or None when absent or when the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    src = os.path.join(ROOT, "long_context_attention_causal_amd", "csrc", source)
+    try:
+        kv = dict(l.split("=", 1) for l in open(path) if "=" in l and not l.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        if kv.get(f"{key}.source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+            return None
+        return float(kv[f"{key}.fetch_bytes"]) + float(kv[f"{key}.write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def dense_flops(B, Hq, N, D):
     return 2.0 * B * Hq * N * N * D
 
@@ -44,7 +60,7 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the 32K/128K dense and 128K sparse lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--long-reps", type=int, default=3)
-    ap.add_argument("--only", choices=["dense", "dense32k", "sparse", "decode"], default=None,
+    ap.add_argument("--only", choices=["dense", "dense32k", "sparse", "decode", "copy"], default=None,
                     help="run one path alone (for profiler runs); prints a short JSON line with its mean time")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -161,6 +177,9 @@ def main():
                                       "pct_bf16_peak_executed": 100 * exec3 / (t_sparse3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                       "dense_equiv_tflops_incl_mask": dense_eq3 / ((t_sparse3 + t_mask3) * 1e-3) / 1e12},
         "decode_paged_c5": {"ms": t_dec, "algorithmic_bytes": dec_bytes, "gbs": dec_gbs,
+                            "measured_hbm_bytes": (lambda a, b: None if a is None or b is None else a + b)(
+                                measured_traffic("decode_split_c5", "decode.hip"),
+                                measured_traffic("decode_combine_c5", "decode.hip")),
                             "pct_hbm_peak": 100 * dec_gbs / PEAK_HBM_GBS, "tokens_per_s": B5 / (t_dec * 1e-3),
                             "tflops": 4.0 * D5 * Hq5 * float(L5.sum()) / (t_dec * 1e-3) / 1e12},
     }
@@ -244,8 +263,10 @@ def main():
                                "(step also runs the N32768 mask+sparse pass and the paged decode)",
                    "global_batch": 1, "seq_len": N, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": tflops2, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops2 / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "prefill_dense_bf16_kernel<128, 8>", "per_launch_flop": fl2},
+                     "frac": tflops2 / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic("prefill_dense_c2", "prefill.hip"),
+                     "kernel": "prefill_dense_bf16_kernel<128, 8>", "per_launch_flop": fl2,
+                     "algorithmic_bytes": float((B * Hq + 2 * c2.k.shape[1]) * N * D * 2 + B * Hq * N * D * 2)},
         "cpu_baseline": cpu,
         "paths": paths,
     }
@@ -253,8 +274,13 @@ def main():
 
 
 def run_only(args, lca, W, torch, np, to_dev, dev):
-    """One path, args.warmup + args.steps calls, for kernel-level profiler runs."""
-    if args.only in ("dense", "dense32k"):
+    """One path, args.warmup + args.steps calls, for kernel-level profiler runs. `copy` is a plain 1 GiB
+    device-to-device copy, the reference for scaling the profiler's HBM byte counters."""
+    if args.only == "copy":
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)
+    elif args.only in ("dense", "dense32k"):
         name = "c2_dense_bf16_n4k" if args.only == "dense" else "c3_sparse_bf16_n32k"
         c = W.make(name)
         q, k, v = to_dev(c.q), to_dev(c.k), to_dev(c.v)
