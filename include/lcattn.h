@@ -122,7 +122,8 @@ attn_status_t attn_block_mask_build(const attn_shape_t* shape, const attn_mask_p
  * rescue branch": the combined mask runs as ordinary block-sparse tiled attention and skipped blocks cost
  * nothing). Lists must be ascending, within [0, i], and hold i itself (every row then sees at least its own
  * key); the kernel trusts them, so the caller validates untrusted lists. kv_count/kv_index as produced by
- * attn_block_mask_build. Supported: bf16, head_dim 64 or 128, block_size a multiple of 64 dividing seq_len.
+ * attn_block_mask_build. Supported: bf16, head_dim 64 or 128, block_size 64, 128 or 256 dividing seq_len, at
+ * most 4096 blocks.
  */
 attn_status_t attn_prefill_block_sparse(const attn_shape_t* shape, int32_t block_size, const void* q,
                                         const void* k, const void* v, const int32_t* kv_count,

@@ -39,28 +39,29 @@ def _compile(src: str, save_temps: bool) -> str:
     return obj
 
 
-def build(jobs: int = 4, save_temps: bool = False, verbose: bool = True) -> str:
+def build(jobs: int = 4, save_temps: bool = False, verbose: bool = True, out: str = LIB) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(lambda s: _compile(s, save_temps), sources()))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     r = subprocess.run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)
     ap.add_argument("--save-temps", action="store_true")
+    ap.add_argument("--out", default=LIB, help="output path of the shared library")
     a = ap.parse_args()
     try:
-        build(a.jobs, a.save_temps)
+        build(a.jobs, a.save_temps, out=os.path.abspath(a.out))
     except RuntimeError as e:
         print(e, file=sys.stderr)
         sys.exit(1)

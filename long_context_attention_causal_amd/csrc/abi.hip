@@ -199,6 +199,7 @@ attn_status_t attn_prefill_block_sparse(const attn_shape_t* shape, int32_t block
     if (block_size != 64 && block_size != 128 && block_size != 256)
         return fail(ATTN_ERR_UNSUPPORTED, "block_size %d is not supported (64, 128 or 256)", block_size);
     if (shape->seq_len % block_size) return fail(ATTN_ERR_SHAPE, "seq_len must be a multiple of block_size");
+    if (shape->seq_len / block_size > 4096) return fail(ATTN_ERR_UNSUPPORTED, "more than 4096 blocks per row");
     if (shape->seq_len == 0) return ok();
     if ((st = check_ptrs({q, k, v, o, kv_count, kv_index})) != ATTN_OK) return st;
     if (lse && !aligned16(lse)) return fail(ATTN_ERR_ALIGN, "lse must be 16-byte aligned");

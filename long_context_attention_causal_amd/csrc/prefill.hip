@@ -27,6 +27,7 @@ namespace lcattn {
 namespace {
 
 constexpr int kBN = 64;        // keys per KV tile
+constexpr int kMaxBlocks = 4096;  // longest kept-block list of one block-sparse row
 constexpr float kSlack = 8.0f; // lazy-rescale threshold, log2 units
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -385,7 +386,8 @@ struct SparseArgs {
 // list (ascending, so the diagonal block, the only one needing an element mask, comes last); skipped blocks
 // are never read. Rows are issued latest block first, as they tend to hold the longest lists.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void prefill_sparse_bf16_kernel(const SparseArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_sparse_bf16_kernel(const SparseArgs a) {
     __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::TILE];
     __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::TILE];
     __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::TILE];
@@ -416,8 +418,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_sparse_bf16_kernel(const Spar
     RowState<D> st;
     init_state<D>(st);
     if (ntiles == 0) return;  // every valid list holds the diagonal; an empty one leaves the rows unwritten
+    // the row's block list goes to LDS once, so the tile loop reads the next tile's block in LDS latency instead
+    // of a global round trip per tile
+    __shared__ int lst[kMaxBlocks];
+    for (int e = tid; e < cnt; e += NW * 64) lst[e] = list[e];
+    __syncthreads();
     const int blk = a.block;
-    attend<D, NW>(tl, krs, vrs, ntiles, [=](int t) { return list[t / sub] * blk + (t % sub) * kBN; }, qf, st, a.c2,
+    attend<D, NW>(tl, krs, vrs, ntiles, [&](int t) { return lst[t / sub] * blk + (t % sub) * kBN; }, qf, st, a.c2,
                   q0, q0 + 31, w, lane);
     finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
 }

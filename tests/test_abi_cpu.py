@@ -113,7 +113,7 @@ def test_mask_workspace_size_and_check(L):
                                    need, None) == 1
 
 
-@pytest.mark.parametrize("blk,N,code", [(32, 128, 3), (64, 100, 2), (512, 1024, 3)])
+@pytest.mark.parametrize("blk,N,code", [(32, 128, 3), (64, 100, 2), (512, 1024, 3), (64, 64 * 4097, 3)])
 def test_sparse_rejects(L, blk, N, code):
     s = shape(N=N)
     assert L.attn_prefill_block_sparse(ctypes.byref(s), blk, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == code
