@@ -98,6 +98,8 @@ attn_status_t check_decode_shape(const attn_decode_shape_t* s, int32_t max_seq_l
         return fail(ATTN_ERR_SHAPE, "batch, heads, max_pages_per_seq must be >= 1 and num_pages >= 0");
     if (s->heads_q % s->heads_kv) return fail(ATTN_ERR_SHAPE, "heads_q must be a multiple of heads_kv");
     if (s->heads_q / s->heads_kv > 16) return fail(ATTN_ERR_UNSUPPORTED, "more than 16 query heads per kv head");
+    if (s->heads_q > 65536) return fail(ATTN_ERR_UNSUPPORTED, "heads_q above 65536");
+    if (s->batch > 65535) return fail(ATTN_ERR_UNSUPPORTED, "batch above 65535");
     if (s->head_dim != 64 && s->head_dim != 128) return fail(ATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     if (s->page_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "page_size must be 16");
     if (s->chunk_tokens < 64 || s->chunk_tokens % 64 || s->chunk_tokens > 4096)
@@ -107,7 +109,7 @@ attn_status_t check_decode_shape(const attn_decode_shape_t* s, int32_t max_seq_l
     if ((long long)max_seq_len > (long long)s->max_pages_per_seq * s->page_size)
         return fail(ATTN_ERR_SHAPE, "max_seq_len exceeds max_pages_per_seq * page_size");
     const long long chunks = ((long long)max_seq_len + s->chunk_tokens - 1) / s->chunk_tokens;
-    if (chunks > 2147483647LL) return fail(ATTN_ERR_SHAPE, "too many chunks");
+    if (chunks * s->heads_kv > 16777215LL) return fail(ATTN_ERR_UNSUPPORTED, "chunks * heads_kv above 16777215");
     return ATTN_OK;
 }
 

@@ -21,19 +21,20 @@ namespace lcattn {
 namespace {
 
 constexpr int kPage = 16;
-constexpr int kPB = 2;   // pages per batch; each wave double-buffers two batches
+// pages per batch; each wave double-buffers two batches. Four pages (32 KiB of K and V per wave in flight at
+// D = 64) stream markedly faster than two, even though the larger V buffers halve the work-groups per CU.
+template <int D>
+constexpr int pages_per_batch() { return D == 64 ? 4 : 2; }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
 struct SplitArgs {
     const uint16_t* q;
     const uint16_t* kc;
     const uint16_t* vc;
     const int32_t* bt;
     const int32_t* lens;
-    float* opart;   // [B, Hq, C, D]
-    float* lpart;   // [B, Hq, C]
+    float* opart;   // [B, C, Hq, D]: a work-group's rows (its kv group's query heads) are one contiguous run
+    float* lpart;   // [B, C, Hq]
     int B, Hq, Hkv, G, max_pages, num_pages, C, chunk, ppw;  // ppw = pages per wave
     float c2;
 };
@@ -46,49 +47,93 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const uint16_t* cach
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, valid * D * 2, 0x00020000);
 }
 
+// One page's transposed V reads (head-dim tiles 32 bytes apart from one lane address), complete on return. They are
+// written as one asm block ending in its own LDS wait because the compiler, when it cannot tell them apart from the
+// direct-to-LDS loads still in flight into the other buffer, would otherwise wait for all of those first.
+typedef __attribute__((address_space(3))) char lds_char;
+template <int DT>
+__device__ __forceinline__ void tr_read_page(v4i16 (&av)[DT], const lds_char* addr);
+template <>
+__device__ __forceinline__ void tr_read_page<4>(v4i16 (&av)[4], const lds_char* addr) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:32\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %4 offset:96\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(av[0]), "=&v"(av[1]), "=&v"(av[2]), "=&v"(av[3])
+        : "v"(addr)
+        : "memory");
+}
+template <>
+__device__ __forceinline__ void tr_read_page<8>(v4i16 (&av)[8], const lds_char* addr) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:160\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:224\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(av[0]), "=&v"(av[1]), "=&v"(av[2]), "=&v"(av[3]), "=&v"(av[4]), "=&v"(av[5]), "=&v"(av[6]),
+          "=&v"(av[7])
+        : "v"(addr)
+        : "memory");
+}
+
 template <int D>
 struct Batch {
-    u32x4 k[kPB][D / 32];   // K slabs straight into the MFMA A-operand layout
+    u32x4 k[pages_per_batch<D>()][D / 32];   // K slabs straight into the MFMA A-operand layout
     int tok0;               // first logical token of the batch
 };
 
-// Work-group = (chunk of chunk_tokens tokens, kv head, sequence); 4 waves, each streaming its ppw pages in
-// batches of kPB pages with the next batch in flight while the current one is used. K goes to VGPRs in the A
+// Work-group = (chunk of chunk_tokens tokens, kv head, sequence); NW waves, each streaming its ppw pages in
+// batches of pages_per_batch pages with the next batch in flight while the current one is used. K goes to VGPRs in the A
 // layout of v_mfma_f32_16x16x32_bf16 (lane = token row, 16-byte pieces of the head dim) and S^T = K Q^T has the
 // kv group's query heads as columns. V goes straight to LDS in its natural layout and comes back as the A
 // operand of v_mfma_f32_16x16x16_bf16 through ds_read_b64_tr_b16 (a 16-lane group receives 16 head-dim rows x 4
 // tokens); the bf16 probabilities are the B operand in the lane that computed them.
-template <int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(const SplitArgs a) {
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_split_kernel(const SplitArgs a) {
     constexpr int KS = D / 32;                    // 16x16x32 MFMAs per page for S^T
     constexpr int DT = D / 16;                    // 16-row tiles of the head dim for O^T
     constexpr int SLAB = kPage * D * 2;           // bytes per page slab
     constexpr int VLOADS = SLAB / 1024;           // 1 KiB direct loads per slab
-    __shared__ __attribute__((aligned(1024))) char vbuf[4][2][kPB * SLAB];   // [wave][buffer]
-    __shared__ float red_m[4][16];
-    __shared__ float red_l[4][16];
+    constexpr int kPB = pages_per_batch<D>();
+    // the two V buffers are distinct arrays: reads of one are then known not to alias direct-to-LDS loads still in
+    // flight into the other, so the compiler does not wait for those loads before reading
+    __shared__ __attribute__((aligned(1024))) char vbuf0[NW][kPB * SLAB];   // [wave]
+    __shared__ __attribute__((aligned(1024))) char vbuf1[NW][kPB * SLAB];
+    __shared__ float red_m[NW][16];
+    __shared__ float red_l[NW][16];
+    static_assert(NW * 16 * D * sizeof(float) <= sizeof(vbuf0), "merge space must fit the first V buffer");
 
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int L = a.lens[b];
-    if (c * a.chunk >= L) return;  // uniform over the work-group
+    const int g = (int)(blockIdx.x % a.Hkv), c = (int)(blockIdx.x / a.Hkv), b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, so page lookups stay scalar
     const int n = lane & 15, grp = lane >> 4;
-
+    // the sequence length, the query rows and the wave's block-table entries (lane i <-> page wpage0 + i, ppw <= 64;
+    // read out later with readlane) are all requested before any of them is waited for; entries past the
+    // sequence end are read but never used
+    const int L = a.lens[b];
+    const int wpage0 = c * (a.chunk / kPage) + w * a.ppw;
+    const int32_t* btrow = a.bt + (size_t)b * a.max_pages;
+    const int my_page = wpage0 + lane;
+    const int my_pid = (lane < a.ppw && my_page < a.max_pages) ? btrow[my_page] : 0;
     bf16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         qf[ks] = n < a.G ? __builtin_bit_cast(bf16x8, load16(a.q + ((size_t)b * a.Hq + g * a.G + n) * D + 32 * ks +
                                                                  8 * grp))
                          : bf16x8{};
+    if (c * a.chunk >= L) return;  // uniform over the work-group
 
     const int npages_seq = (L + kPage - 1) / kPage;
-    const int wpage0 = c * (a.chunk / kPage) + w * a.ppw;
-    const int32_t* btrow = a.bt + (size_t)b * a.max_pages;
-    const int nbatch = (a.ppw + kPB - 1) / kPB;
-    // the wave's block-table entries in one load (lane i <-> page wpage0 + i; ppw <= 64), read out with readlane
-    const int my_page = wpage0 + lane;
-    const int my_pid = (lane < a.ppw && my_page < npages_seq && my_page < a.max_pages) ? btrow[my_page] : 0;
+    // an even batch count, so the loop below runs both buffers every trip; batches past the wave's pages read
+    // zeros through empty buffer views and are masked
+    const int nbatch = ((a.ppw + 2 * kPB - 1) / (2 * kPB)) * 2;
 
     // issue batch `bi` into buffer `buf`
     auto issue = [&](int bi, int buf, Batch<D>& bt) {
@@ -97,7 +142,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const SplitArgs a) {
         for (int p = 0; p < kPB; ++p) {
             const int lp = wpage0 + bi * kPB + p;
             const bool inrange = bi * kPB + p < a.ppw && lp < npages_seq && lp < a.max_pages;
-            int pid = inrange ? __builtin_amdgcn_readlane(my_pid, bi * kPB + p) : 0;
+            int pid = inrange ? __builtin_amdgcn_readlane(my_pid, min(bi * kPB + p, 63)) : 0;
             int valid = inrange ? min(kPage, L - lp * kPage) : 0;
             if ((unsigned)pid >= (unsigned)a.num_pages) {
                 pid = 0;
@@ -109,7 +154,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const SplitArgs a) {
             for (int ks = 0; ks < KS; ++ks)
                 bt.k[p][ks] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, (n * D + 32 * ks + 8 * grp) * 2, 0, 0));
-            lds_char* dst = (lds_char*)&vbuf[w][buf][p * SLAB];
+            lds_char* dst = (buf ? (lds_char*)&vbuf1[w][0] : (lds_char*)&vbuf0[w][0]) + p * SLAB;
 #pragma unroll
             for (int i = 0; i < VLOADS; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(dst + i * 1024),
@@ -125,14 +170,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const SplitArgs a) {
     ones[0] = (__bf16)1.0f;
     ones[1] = (__bf16)1.0f;
 
-    // one batch: issue the next batch into the other register set and LDS buffer, wait for this one, use it
+    // one batch: issue the next batch into the other register set and LDS buffer (an empty one past the last), wait
+    // for this one, use it. The issue and the wait are unconditional so that the only loads still outstanding
+    // during the maths are the next batch's, whatever the path.
     auto run = [&](int bi, int buf, Batch<D>& cur, Batch<D>& nxt) {
-        if (bi + 1 < nbatch) {
-            issue(bi + 1, buf ^ 1, nxt);
-            __builtin_amdgcn_s_waitcnt(0x0F70 | ((KS + VLOADS) * kPB & 15) | ((((KS + VLOADS) * kPB) >> 4) << 14));
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        }
+        issue(bi + 1, buf ^ 1, nxt);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | ((KS + VLOADS) * kPB & 15) | ((((KS + VLOADS) * kPB) >> 4) << 14));
         // scores S^T[token = 4*grp + r][head n] per page
         f32x4 s[kPB];
         float mx = -INFINITY;
@@ -177,14 +220,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const SplitArgs a) {
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, l, false);
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, l, false);
             // source lane 4*jj + aa of 16-lane group grp points at V[token 4*grp + jj][16*dt + 4*aa]
-            const lds_char* slab = (const lds_char*)&vbuf[w][buf][p * SLAB];
+            const lds_char* slab = (buf ? (const lds_char*)&vbuf1[w][0] : (const lds_char*)&vbuf0[w][0]) + p * SLAB;
             const int src = (4 * grp + ((lane & 15) >> 2)) * D * 2 + 8 * (lane & 3);
+            v4i16 av[DT];
+            tr_read_page<DT>(av, slab + src);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-                const v4i16 av = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(slab + src + 32 * dt));
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, av), pb, o[dt], 0, 0, 0);
-            }
+            for (int dt = 0; dt < DT; ++dt)
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, av[dt]), pb, o[dt], 0, 0,
+                                                                   0);
         }
         // all lanes are done reading this buffer before the next batch's loads may target it
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -196,14 +239,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const SplitArgs a) {
     issue(0, 0, ba);
     for (int bi = 0; bi < nbatch; bi += 2) {
         run(bi, 0, ba, bb);
-        if (bi + 1 < nbatch) run(bi + 1, 1, bb, ba);
+        run(bi + 1, 1, bb, ba);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // the empty batch issued last targets the first V buffer, reused below
     // wave partial -> LDS: this lane holds O^T[d = 16*dt + 4*grp + r][head n], sum share l, max m (same over a
     // head's lanes)
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     __syncthreads();  // every wave is done with its V buffers; reuse the space for the merge
-    float* red_o = reinterpret_cast<float*>(&vbuf[0][0][0]);  // [4 waves][16 heads][D]
+    float* red_o = reinterpret_cast<float*>(&vbuf0[0][0]);  // [NW waves][16 heads][D]
     if (grp == 0) {
         red_m[w][n] = m;
         red_l[w][n] = l;
@@ -213,21 +257,23 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const SplitArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) red_o[(w * 16 + n) * D + 16 * dt + 4 * grp + r] = o[dt][r];
     __syncthreads();
-    for (int e = tid; e < a.G * D; e += 256) {
-        const int hn = e / D, d = e % D;
+    // each thread finishes four consecutive head dims of one head and stores them as one 16-byte write
+    for (int e = tid; e < a.G * (D / 4); e += NW * 64) {
+        const int hn = e / (D / 4), d = 4 * (e % (D / 4));
         float M = red_m[0][hn];
 #pragma unroll
-        for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, red_m[ww][hn]);
-        float acc = 0.0f, lsum = 0.0f;
+        for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, red_m[ww][hn]);
+        f32x4 acc = f32x4{};
+        float lsum = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
+        for (int ww = 0; ww < NW; ++ww) {
             const float mw = red_m[ww][hn];
             const float sc = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-            acc += sc * red_o[(ww * 16 + hn) * D + d];
+            acc += sc * *reinterpret_cast<const f32x4*>(&red_o[(ww * 16 + hn) * D + d]);
             lsum += sc * red_l[ww][hn];
         }
-        const size_t row = ((size_t)b * a.Hq + g * a.G + hn) * a.C + c;
-        a.opart[row * D + d] = acc / lsum;
+        const size_t row = ((size_t)b * a.C + c) * a.Hq + g * a.G + hn;
+        *reinterpret_cast<f32x4*>(&a.opart[row * D + d]) = acc * (1.0f / lsum);
         if (d == 0) a.lpart[row] = (M + log2f(lsum)) * kLn2;
     }
 }
@@ -241,58 +287,62 @@ struct CombineArgs {
     int B, Hq, C, chunk;
 };
 
+// One wave per (sequence, query head). The chunk rows are fetched with 16-byte loads that each cover 64 / (D / 4)
+// rows, all rows of a group of 64 chunks in flight at once (a buffer view clipped at the last chunk reads zeros
+// past it); lane c holds chunk c's log-sum-exp, and each row's weight reaches the lanes that loaded it by shuffle.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const CombineArgs a) {
+    constexpr int LPR = D / 4;      // lanes per partial row
+    constexpr int RPL = 64 / LPR;   // partial rows per wave load
+    constexpr int NL = 64 / RPL;    // loads per group of 64 chunks
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int bh = blockIdx.x * 4 + w;
     if (bh >= a.B * a.Hq) return;
-    const int b = bh / a.Hq;
+    const int b = bh / a.Hq, h = bh % a.Hq;
     const int L = a.lens[b];
     const int nc = min(a.C, (L + a.chunk - 1) / a.chunk);
-    const float* lp = a.lpart + (size_t)bh * a.C;
-    const float* op = a.opart + (size_t)bh * a.C * D;
+    // chunk c of this (sequence, head) sits at row (b * C + c) * Hq + h
+    const float* lp = a.lpart + (size_t)b * a.C * a.Hq + h;
+    const float* op = a.opart + ((size_t)b * a.C * a.Hq + h) * D;
+    const int hs = a.Hq;
     uint16_t* orow = a.o + (size_t)bh * D;
     if (nc == 0) {
         for (int d = lane; d < D; d += 64) orow[d] = 0;
         if (a.lse && lane == 0) a.lse[bh] = -INFINITY;
         return;
     }
-    // chunk weights: lane c holds chunk c (and c + 64, ...)
-    float M = -INFINITY;
-    for (int c0 = 0; c0 < nc; c0 += 64) M = fmaxf(M, c0 + lane < nc ? lp[c0 + lane] : -INFINITY);
+    const int rr = lane / LPR, dq = 4 * (lane % LPR);
+    const float lp0 = lane < nc ? lp[(size_t)lane * hs] : -INFINITY;
+    float M = lp0;
+    for (int c0 = 64; c0 < nc; c0 += 64) M = fmaxf(M, c0 + lane < nc ? lp[(size_t)(c0 + lane) * hs] : -INFINITY);
     M = wave_max(M);
-    float acc[D / 64];
-#pragma unroll
-    for (int k = 0; k < D / 64; ++k) acc[k] = 0.0f;
+    f32x4 acc = f32x4{};
     float sw = 0.0f;
     for (int c0 = 0; c0 < nc; c0 += 64) {
-        const float wl = c0 + lane < nc ? expf(lp[c0 + lane] - M) : 0.0f;
+        const int rows = min(64, nc - c0);
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(op + (size_t)c0 * hs * D), (short)0, ((rows - 1) * hs * D + D) * 4, 0x00020000);
+        f32x4 v[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            v[i] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((RPL * i + rr) * hs * D + dq) * 4, 0, 0));
+        const float lv = c0 == 0 ? lp0 : (c0 + lane < nc ? lp[(size_t)(c0 + lane) * hs] : -INFINITY);
+        const float wl = lv == -INFINITY ? 0.0f : expf(lv - M);
         sw += wl;
-        const int cn = min(64, nc - c0);
-        int c = 0;
-        for (; c + 8 <= cn; c += 8) {
-            float v[8][D / 64];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-                for (int k = 0; k < D / 64; ++k) v[u][k] = op[(size_t)(c0 + c + u) * D + lane + 64 * k];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float wc = __shfl(wl, c + u);
-#pragma unroll
-                for (int k = 0; k < D / 64; ++k) acc[k] = __builtin_fmaf(wc, v[u][k], acc[k]);
-            }
-        }
-        for (; c < cn; ++c) {
-            const float wc = __shfl(wl, c);
-#pragma unroll
-            for (int k = 0; k < D / 64; ++k) acc[k] = __builtin_fmaf(wc, op[(size_t)(c0 + c) * D + lane + 64 * k], acc[k]);
-        }
+        for (int i = 0; i < NL; ++i) acc += __shfl(wl, RPL * i + rr) * v[i];
     }
+#pragma unroll
+    for (int sh = LPR; sh < 64; sh <<= 1)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] += __shfl_xor(acc[k], sh);
     sw = wave_sum(sw);
     const float inv = 1.0f / sw;
-#pragma unroll
-    for (int k = 0; k < D / 64; ++k) orow[lane + 64 * k] = __builtin_bit_cast(uint16_t, (__bf16)(acc[k] * inv));
+    if (rr == 0) {
+        const uint32_t w0 = pack_bf16x2(acc[0] * inv, acc[1] * inv), w1 = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+        *reinterpret_cast<u32x2*>(orow + dq) = u32x2{w0, w1};
+    }
     if (a.lse && lane == 0) a.lse[bh] = M + logf(sw);
 }
 
@@ -324,12 +374,23 @@ hipError_t launch_decode_paged(const DecodeProblem& p, void* workspace, hipStrea
     a.num_pages = p.num_pages;
     a.C = C ? C : 1;
     a.chunk = p.chunk;
-    a.ppw = p.chunk / kPage / 4;
+    // one wave per chunk up to 64 pages, so each wave streams as long a run of pages as it can hold block-table
+    // entries for (one per lane); longer chunks are shared by 2 or 4 waves
+    const int nw = p.chunk <= 64 * kPage ? 1 : p.chunk <= 128 * kPage ? 2 : 4;
+    a.ppw = p.chunk / kPage / nw;
     a.c2 = p.scale * kLog2e;
     if (C > 0) {
-        const dim3 grid((unsigned)C, (unsigned)p.Hkv, (unsigned)p.B);
-        if (p.D == 64) hipLaunchKernelGGL((decode_split_kernel<64>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((decode_split_kernel<128>), grid, dim3(256), 0, s, a);
+        const dim3 grid((unsigned)(C * p.Hkv), (unsigned)p.B);   // kv head fastest: neighbours share pages
+        const dim3 block((unsigned)(nw * 64));
+        if (p.D == 64) {
+            if (nw == 1) hipLaunchKernelGGL((decode_split_kernel<64, 1>), grid, block, 0, s, a);
+            else if (nw == 2) hipLaunchKernelGGL((decode_split_kernel<64, 2>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((decode_split_kernel<64, 4>), grid, block, 0, s, a);
+        } else {
+            if (nw == 1) hipLaunchKernelGGL((decode_split_kernel<128, 1>), grid, block, 0, s, a);
+            else if (nw == 2) hipLaunchKernelGGL((decode_split_kernel<128, 2>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((decode_split_kernel<128, 4>), grid, block, 0, s, a);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

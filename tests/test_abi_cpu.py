@@ -142,6 +142,9 @@ def dshape(B=4, Hq=16, Hkv=2, D=64, page=16, maxp=64, pages=100, chunk=512, scal
     (dshape(), -1, 2),
     (dshape(scale=-1.0), 100, 2),
     (dshape(pages=0), 100, 2),
+    (dshape(B=65536), 100, 3),
+    (dshape(Hq=4096, Hkv=4096, chunk=64, maxp=300000), 4097 * 64, 3),
+    (dshape(Hq=16 * 4097, Hkv=4097), 100, 3),
 ])
 def test_decode_rejects(L, s, maxlen, code):
     assert L.attn_decode_paged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, maxlen, FAKE, None, FAKE, 1 << 40,
