@@ -21,11 +21,6 @@ namespace lcattn {
 namespace {
 
 constexpr int kPage = 16;
-// pages per batch; each wave double-buffers two batches. Four pages (32 KiB of K and V per wave in flight at
-// D = 64) stream markedly faster than two, even though the larger V buffers halve the work-groups per CU.
-template <int D>
-constexpr int pages_per_batch() { return D == 64 ? 4 : 2; }
-
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 struct SplitArgs {
     const uint16_t* q;
@@ -83,32 +78,31 @@ __device__ __forceinline__ void tr_read_page<8>(v4i16 (&av)[8], const lds_char* 
         : "memory");
 }
 
-template <int D>
+template <int D, int PB>
 struct Batch {
-    u32x4 k[pages_per_batch<D>()][D / 32];   // K slabs straight into the MFMA A-operand layout
+    u32x4 k[PB][D / 32];   // K slabs straight into the MFMA A-operand layout
     int tok0;               // first logical token of the batch
 };
 
 // Work-group = (chunk of chunk_tokens tokens, kv head, sequence); NW waves, each streaming its ppw pages in
-// batches of pages_per_batch pages with the next batch in flight while the current one is used. K goes to VGPRs in the A
+// batches of PB pages with the next batch in flight while the current one is used. K goes to VGPRs in the A
 // layout of v_mfma_f32_16x16x32_bf16 (lane = token row, 16-byte pieces of the head dim) and S^T = K Q^T has the
 // kv group's query heads as columns. V goes straight to LDS in its natural layout and comes back as the A
 // operand of v_mfma_f32_16x16x16_bf16 through ds_read_b64_tr_b16 (a 16-lane group receives 16 head-dim rows x 4
 // tokens); the bf16 probabilities are the B operand in the lane that computed them.
-template <int D, int NW>
+template <int D, int NW, int PB>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(const SplitArgs a) {
     constexpr int KS = D / 32;                    // 16x16x32 MFMAs per page for S^T
     constexpr int DT = D / 16;                    // 16-row tiles of the head dim for O^T
     constexpr int SLAB = kPage * D * 2;           // bytes per page slab
     constexpr int VLOADS = SLAB / 1024;           // 1 KiB direct loads per slab
-    constexpr int kPB = pages_per_batch<D>();
+    constexpr int kPB = PB;
     // the two V buffers are distinct arrays: reads of one are then known not to alias direct-to-LDS loads still in
     // flight into the other, so the compiler does not wait for those loads before reading
     __shared__ __attribute__((aligned(1024))) char vbuf0[NW][kPB * SLAB];   // [wave]
     __shared__ __attribute__((aligned(1024))) char vbuf1[NW][kPB * SLAB];
-    __shared__ float red_m[NW][16];
-    __shared__ float red_l[NW][16];
-    static_assert(NW * 16 * D * sizeof(float) <= sizeof(vbuf0), "merge space must fit the first V buffer");
+    static_assert(NW * 16 * D * sizeof(float) <= sizeof(vbuf0), "merge partials must fit the first V buffer");
+    static_assert(2 * NW * 16 * sizeof(float) <= sizeof(vbuf1), "merge maxima and sums must fit the second");
 
     const int g = (int)(blockIdx.x % a.Hkv), c = (int)(blockIdx.x / a.Hkv), b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -136,7 +130,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(const SplitArgs a
     const int nbatch = ((a.ppw + 2 * kPB - 1) / (2 * kPB)) * 2;
 
     // issue batch `bi` into buffer `buf`
-    auto issue = [&](int bi, int buf, Batch<D>& bt) {
+    auto issue = [&](int bi, int buf, Batch<D, PB>& bt) {
         bt.tok0 = (wpage0 + bi * kPB) * kPage;
 #pragma unroll
         for (int p = 0; p < kPB; ++p) {
@@ -173,7 +167,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(const SplitArgs a
     // one batch: issue the next batch into the other register set and LDS buffer (an empty one past the last), wait
     // for this one, use it. The issue and the wait are unconditional so that the only loads still outstanding
     // during the maths are the next batch's, whatever the path.
-    auto run = [&](int bi, int buf, Batch<D>& cur, Batch<D>& nxt) {
+    auto run = [&](int bi, int buf, Batch<D, PB>& cur, Batch<D, PB>& nxt) {
         issue(bi + 1, buf ^ 1, nxt);
         __builtin_amdgcn_s_waitcnt(0x0F70 | ((KS + VLOADS) * kPB & 15) | ((((KS + VLOADS) * kPB) >> 4) << 14));
         // scores S^T[token = 4*grp + r][head n] per page
@@ -235,7 +229,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(const SplitArgs a
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    Batch<D> ba, bb;
+    Batch<D, PB> ba, bb;
     issue(0, 0, ba);
     for (int bi = 0; bi < nbatch; bi += 2) {
         run(bi, 0, ba, bb);
@@ -247,7 +241,11 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(const SplitArgs a
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     __syncthreads();  // every wave is done with its V buffers; reuse the space for the merge
-    float* red_o = reinterpret_cast<float*>(&vbuf0[0][0]);  // [NW waves][16 heads][D]
+    // the merge reuses the V buffers: partial outputs [NW waves][16 heads][D] in the first, maxima and sums in the
+    // second
+    float* red_o = reinterpret_cast<float*>(&vbuf0[0][0]);
+    float (*red_m)[16] = reinterpret_cast<float (*)[16]>(&vbuf1[0][0]);
+    float (*red_l)[16] = red_m + NW;
     if (grp == 0) {
         red_m[w][n] = m;
         red_l[w][n] = l;
@@ -346,6 +344,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const CombineArgs a
     if (a.lse && lane == 0) a.lse[bh] = M + logf(sw);
 }
 
+template <int D, int NW>
+void launch_split(int pb, dim3 grid, const SplitArgs& a, hipStream_t s) {
+    const dim3 block(NW * 64);
+    if (pb == 2) hipLaunchKernelGGL((decode_split_kernel<D, NW, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<D, NW, 4>), grid, block, 0, s, a);
+}
+
+template <int D>
+void launch_split(int nw, int pb, dim3 grid, const SplitArgs& a, hipStream_t s) {
+    if (nw == 1) launch_split<D, 1>(pb, grid, a, s);
+    else if (nw == 2) launch_split<D, 2>(pb, grid, a, s);
+    else launch_split<D, 4>(pb, grid, a, s);
+}
+
 }  // namespace
 
 size_t decode_workspace_bytes(int B, int Hq, int D, int chunk, int max_seq_len) {
@@ -374,23 +386,18 @@ hipError_t launch_decode_paged(const DecodeProblem& p, void* workspace, hipStrea
     a.num_pages = p.num_pages;
     a.C = C ? C : 1;
     a.chunk = p.chunk;
-    // one wave per chunk up to 64 pages, so each wave streams as long a run of pages as it can hold block-table
-    // entries for (one per lane); longer chunks are shared by 2 or 4 waves
-    const int nw = p.chunk <= 64 * kPage ? 1 : p.chunk <= 128 * kPage ? 2 : 4;
+    // waves per work-group and pages per batch: about 16 pages per wave (all shapes from 8 to 32 pages per wave and
+    // 2 or 4 pages per batch measured within 3% of each other on the paged workload, this one at the front); a wave
+    // holds at most 64 pages' block-table entries, one per lane, which 4 waves reach at the largest chunk
+    const int pages = p.chunk / kPage;
+    const int nw = pages <= 16 ? 1 : pages <= 32 ? 2 : 4;
+    const int pb = p.D == 64 ? 4 : 2;
     a.ppw = p.chunk / kPage / nw;
     a.c2 = p.scale * kLog2e;
     if (C > 0) {
         const dim3 grid((unsigned)(C * p.Hkv), (unsigned)p.B);   // kv head fastest: neighbours share pages
-        const dim3 block((unsigned)(nw * 64));
-        if (p.D == 64) {
-            if (nw == 1) hipLaunchKernelGGL((decode_split_kernel<64, 1>), grid, block, 0, s, a);
-            else if (nw == 2) hipLaunchKernelGGL((decode_split_kernel<64, 2>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((decode_split_kernel<64, 4>), grid, block, 0, s, a);
-        } else {
-            if (nw == 1) hipLaunchKernelGGL((decode_split_kernel<128, 1>), grid, block, 0, s, a);
-            else if (nw == 2) hipLaunchKernelGGL((decode_split_kernel<128, 2>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((decode_split_kernel<128, 4>), grid, block, 0, s, a);
-        }
+        if (p.D == 64) launch_split<64>(nw, pb, grid, a, s);
+        else launch_split<128>(nw, pb, grid, a, s);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

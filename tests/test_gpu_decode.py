@@ -61,10 +61,12 @@ def test_edges(lib, lens, D, G):
     compare(lib, d, f"edges D={D} G={G}")
 
 
-@pytest.mark.parametrize("chunk", [64, 128, 1024])
-def test_split_sizes_agree_with_oracle(lib, chunk):
-    d = W.decode_inputs(33, 6, 16, 2, 64, 16, 1, 3000)
-    compare(lib, d, "split", chunk=chunk)
+# chunk sizes that select every launch shape: one, two and four waves per work-group, both head dims
+@pytest.mark.parametrize("chunk,D", [(64, 64), (128, 64), (1024, 64), (4096, 64), (64, 128), (512, 128), (1024, 128),
+                                     (4096, 128)])
+def test_split_sizes_agree_with_oracle(lib, chunk, D):
+    d = W.decode_inputs(33, 6, 16, 2, D, 16, 1, 5000)
+    compare(lib, d, f"split D={D}", chunk=chunk)
 
 
 def test_split_vs_unsplit_on_gpu(lib):
