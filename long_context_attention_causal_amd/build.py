@@ -23,6 +23,11 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops", "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
 
+# Per-source extras. The prefill kernels' row maxima see no NaN unless the inputs hold one (the output is then NaN
+# regardless), so they are built without NaN semantics: a max then needs no quieting of its inputs, which otherwise
+# doubles the VALU work of every tile's row-max reduction. Infinities keep their meaning (masked scores are -inf).
+EXTRA = {"prefill.hip": ["-fno-honor-nans"]}
+
 
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
@@ -30,7 +35,7 @@ def sources():
 
 def _compile(src: str, save_temps: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = ["hipcc", *COMMON, "-c", src, "-o", obj]
+    cmd = ["hipcc", *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if save_temps:
         cmd.append("--save-temps")
     r = subprocess.run(cmd, cwd=BUILD, capture_output=True, text=True)

@@ -27,54 +27,72 @@ namespace lcattn {
 namespace {
 
 constexpr int kBN = 64;        // keys per KV tile
-constexpr int kMaxBlocks = 4096;  // longest kept-block list of one block-sparse row
 constexpr float kSlack = 8.0f; // lazy-rescale threshold, log2 units
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-// K and V tiles (64 keys x D, bf16) live in LDS in their natural row-major layout without padding; 16-byte chunk c
-// of row r sits at chunk position c ^ swz(r). The swizzle keeps both access patterns free of bank conflicts:
-// the 16-byte K reads of 16 consecutive rows, and the 8-byte transposed V reads of four consecutive keys.
+// K and V tiles (64 keys x D, bf16) live in LDS row-major with padded row strides chosen for gfx950's LDS, whose 64
+// four-byte banks span 256 bytes, i.e. 16 slots of 16 bytes:
+//   - a 16-byte K read serves 16 lanes at a time: 16 consecutive rows at one chunk. A K row stride of an odd number
+//     of 16-byte chunks (D/8 + 1) puts them on 16 distinct slots.
+//   - a transposed V read serves 32 lanes at a time: 4 consecutive keys (the first a multiple of 4) x 4 consecutive
+//     chunks (likewise). A V row stride of D/8 + 4 chunks, i.e. 4 (D = 128) or 12 (D = 64) modulo 16, moves the
+//     four keys' chunk groups onto four disjoint groups of slots.
+// Both reads are then a per-lane base plus a compile-time offset, with no address arithmetic per read. (An XOR
+// swizzle of the unpadded rows can avoid the conflicts too, but costs address work per read and registers.)
 template <int D>
 struct Lds {
-    static constexpr int ROWB = D * 2;            // bytes per key row
-    static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
-    static constexpr int TILE = kBN * ROWB;       // one K or V tile
-    static constexpr int LOADS = TILE / 1024;     // 64-lane x 16-byte direct loads per tile
-    __device__ static __forceinline__ int swz(int r) {
-        return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
-    }
+    static constexpr int ROWB = D * 2;              // bytes per key row in HBM
+    static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
+    static constexpr int KSTR = ROWB + 16;          // LDS row stride of a K tile
+    static constexpr int VSTR = ROWB + 64;          // LDS row stride of a V tile
+    static constexpr int KTILE = kBN * KSTR;        // bytes of one K tile (a multiple of 1 KiB)
+    static constexpr int VTILE = kBN * VSTR;
+    static_assert(KTILE % 1024 == 0 && VTILE % 1024 == 0, "tiles are filled by whole 1 KiB direct loads");
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, bytes, 0x00020000);
 }
 
-// Direct global->LDS staging of one tile by the work-group's NW waves: each 64-lane load moves 1 KiB into
-// consecutive LDS bytes, lane l's 16 bytes to position l; the lane fetches the global chunk that the swizzle puts
-// there. Buffer range checking returns zeros for keys outside [0, N) (including negative tile starts).
-template <int D, int NW>
+// Direct global->LDS staging of one tile (row stride STR in LDS) by the work-group's NW waves: each 64-lane load
+// moves 1 KiB into consecutive LDS bytes, lane l's 16 bytes to position l; the lane fetches the global chunk that
+// lands there (a padding slot re-reads a chunk of the same row, so it costs no extra memory traffic). Buffer range
+// checking returns zeros for keys outside [0, N) (including negative tile starts).
+template <int D, int NW, int STR>
 struct TileLoader {
-    static constexpr int PER = (Lds<D>::LOADS + NW - 1) / NW;
+    static constexpr int LOADS = kBN * STR / 1024;
+    static constexpr int PER = (LOADS + NW - 1) / NW;
+    static constexpr int SPR = STR / 16;   // 16-byte slots per LDS row
     int voff[PER];
     int first;   // this wave's first load slot
     __device__ __forceinline__ void init(int w, int lane) {
         first = w * PER;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int z = (first + i) * 64 + lane;           // 16-byte slot inside the tile
-            const int r = z / Lds<D>::CPR, pc = z % Lds<D>::CPR;
-            voff[i] = r * Lds<D>::ROWB + ((pc ^ Lds<D>::swz(r)) * 16);
+            const int z = (first + i) * 64 + lane;   // 16-byte slot inside the tile
+            const int r = z / SPR, c = z % SPR;
+            voff[i] = r * Lds<D>::ROWB + min(c, Lds<D>::CPR - 1) * 16;
         }
     }
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int kv0) const {
         const int soff = kv0 * Lds<D>::ROWB;
 #pragma unroll
         for (int i = 0; i < PER; ++i)
-            if (Lds<D>::LOADS % NW == 0 || first + i < Lds<D>::LOADS)
+            if (LOADS % NW == 0 || first + i < LOADS)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + (first + i) * 1024),
                                                          16, voff[i], soff, 0, 0);
+    }
+};
+
+template <int D, int NW>
+struct Loaders {
+    TileLoader<D, NW, Lds<D>::KSTR> k;
+    TileLoader<D, NW, Lds<D>::VSTR> v;
+    __device__ __forceinline__ void init(int w, int lane) {
+        k.init(w, lane);
+        v.init(w, lane);
     }
 };
 
@@ -99,7 +117,7 @@ __device__ __forceinline__ void qk_tile(const lds_char* kl, const bf16x8 (&qf)[D
         for (int t = 0; t < 2; ++t) {
             const int r = 32 * t + ln;
             const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-                kl + r * Lds<D>::ROWB + (((2 * ks + hi) ^ Lds<D>::swz(r)) * 16));
+                kl + r * Lds<D>::KSTR + (2 * ks + hi) * 16);
             s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
         }
 }
@@ -115,11 +133,11 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Online-softmax update for one tile: row max (lazy refresh), probabilities rounded to bf16 and packed in the
-// B-operand order of the PV product, row-sum share updated with the rounded values.
+// Online-softmax update for one tile, first half: element mask on a diagonal tile, row max, lazy refresh of the
+// running max (rescaling O and the sum when it moves by more than kSlack). Returns the exp2 bias.
 template <int D>
-__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], uint32_t (&pw)[2][8], RowState<D>& st, float c2,
-                                             bool diag, int kv0, int qrow, int lane) {
+__device__ __forceinline__ float softmax_max(f32x16 (&s)[2], RowState<D>& st, float c2, bool diag, int kv0, int qrow,
+                                             int lane) {
     const int hi = lane >> 5;
     if (diag) {
 #pragma unroll
@@ -145,21 +163,32 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], uint32_t (&pw)[2][8
         for (int dt = 0; dt < D / 32; ++dt) st.o[dt] *= alpha;
         st.m = mxs;
     }
-    const float bias = (st.m == -INFINITY) ? 0.0f : -st.m;
+    return (st.m == -INFINITY) ? 0.0f : -st.m;
+}
+
+// Second half, one slice: the two probabilities of accumulator slots 2w and 2w+1 of key half t, rounded to bf16 and
+// packed in the B-operand order of the PV product; their sum (of the rounded values) goes into l.
+__device__ __forceinline__ void softmax_slice(const f32x16 (&s)[2], uint32_t (&pw)[2][8], int t, int w, float c2,
+                                              float bias, float& l) {
     bf16x2 ones;
     ones[0] = (__bf16)1.0f;
     ones[1] = (__bf16)1.0f;
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * w], c2, bias));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * w + 1], c2, bias));
+    pw[t][w] = pack_bf16x2(p0, p1);
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[t][w]), ones, l, false);
+}
+
+// Whole online-softmax update for one tile.
+template <int D>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], uint32_t (&pw)[2][8], RowState<D>& st, float c2,
+                                             bool diag, int kv0, int qrow, int lane) {
+    const float bias = softmax_max<D>(s, st, c2, diag, kv0, qrow, lane);
     float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * w], c2, bias));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * w + 1], c2, bias));
-            pw[t][w] = pack_bf16x2(p0, p1);
-            if (w & 1) l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[t][w]), ones, l1, false);
-            else l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[t][w]), ones, l0, false);
-        }
+        for (int w = 0; w < 8; ++w) softmax_slice(s, pw, t, w, c2, bias, (w & 1) ? l1 : l0);
     st.l += l0 + l1;
 }
 
@@ -176,7 +205,7 @@ struct VtAddr {
         dq = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     }
     __device__ __forceinline__ int at(int key, int d) const {
-        return key * Lds<D>::ROWB + (((d >> 3) ^ Lds<D>::swz(key)) * 16) + (d & 7) * 2;
+        return key * Lds<D>::VSTR + d * 2;
     }
 };
 
@@ -203,6 +232,68 @@ __device__ __forceinline__ void pv_tile(const lds_char* vl, const VtAddr<D>& va,
                 st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, st.o[dt], 0, 0, 0);
             }
         }
+}
+
+// Steady-state tile with a fixed schedule: tile j's softmax, tile j+1's QK and tile j's PV in one stream of steps
+// separated by hard scheduling barriers, so the order below is the issue order. QK step i: the K read two MFMAs
+// ahead, the MFMA, and 16 / (D / 8) slices of the softmax on the VALU (they only need the row max, computed
+// first). PV step j: the two transposed reads of the MFMA two ahead, then the MFMA. Every MFMA finds its operands
+// already requested two steps earlier, and the VALU work fills the matrix cores' busy time.
+template <int D>
+__device__ __forceinline__ void steady_tile(const lds_char* kl, const lds_char* vl, const VtAddr<D>& va,
+                                            const bf16x8 (&qf)[D / 16], f32x16 (&scur)[2], f32x16 (&snext)[2],
+                                            uint32_t (&pw)[2][8], RowState<D>& st, float c2, int qrow, int lane) {
+    constexpr int NQK = D / 8;        // (D / 16) k-steps x 2 key halves
+    constexpr int SPQ = 16 / NQK;     // softmax slices per QK MFMA
+    constexpr int NPV = D / 8;        // 2 key halves x 2 16-key slices x (D / 32) head-dim tiles
+    constexpr int AH = 2;             // reads issued this many MFMAs ahead
+    const int hi = lane >> 5, ln = lane & 31;
+    const float bias = softmax_max<D>(scur, st, c2, false, 0, qrow, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    auto kread = [&](int i) {
+        const int ks = i >> 1, r = 32 * (i & 1) + ln;
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kl + r * Lds<D>::KSTR + (2 * ks + hi) * 16);
+    };
+    bf16x8 kf[NQK];
+    snext[0] = f32x16{};
+    snext[1] = f32x16{};
+    float l0 = 0.0f, l1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < AH; ++i) kf[i] = kread(i);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+        if (i + AH < NQK) kf[i + AH] = kread(i + AH);
+        snext[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], snext[i & 1], 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < SPQ; ++k) {
+            const int sl = i * SPQ + k;
+            softmax_slice(scur, pw, sl >> 3, sl & 7, c2, bias, (sl & 1) ? l1 : l0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    st.l += l0 + l1;
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    auto vread = [&](int j, v4i16& lo, v4i16& hi4) {
+        const int t = j / (2 * (D / 32)), u = (j / (D / 32)) & 1, dt = j % (D / 32);
+        const int key = 32 * t + 16 * u + va.key_lo, d = 32 * dt + va.dq;
+        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + va.at(key, d)));
+        hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + va.at(key + 8, d)));
+    };
+    v4i16 vlo[NPV], vhi[NPV];
+#pragma unroll
+    for (int j = 0; j < AH; ++j) vread(j, vlo[j], vhi[j]);
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) {
+        if (j + AH < NPV) vread(j + AH, vlo[j + AH], vhi[j + AH]);
+        const int t = j / (2 * (D / 32)), u = (j / (D / 32)) & 1, dt = j % (D / 32);
+        const bf16x8 b = __builtin_bit_cast(
+            bf16x8, (u32x4{pw[t][4 * u], pw[t][4 * u + 1], pw[t][4 * u + 2], pw[t][4 * u + 3]}));
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, (u32x4{__builtin_bit_cast(u32x2, vlo[j])[0], __builtin_bit_cast(u32x2, vlo[j])[1],
+                           __builtin_bit_cast(u32x2, vhi[j])[0], __builtin_bit_cast(u32x2, vhi[j])[1]}));
+        st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, st.o[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 template <int D>
@@ -257,7 +348,7 @@ struct Tiles {
 // kv_of(t) gives tile t's first key; a wave skips tiles that start past its last row, and masks elements only on
 // tiles that reach past its first row.
 template <int D, int NW, int PAR, typename KvOf>
-__device__ __forceinline__ void attend_step(const Tiles<D>& tl, const TileLoader<D, NW>& ld,
+__device__ __forceinline__ void attend_step(const Tiles<D>& tl, const Loaders<D, NW>& ld,
                                             __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, const VtAddr<D>& va,
                                             int j, int ntiles, KvOf kv_of, int& kv_cur, int& kv_nxt,
                                             const bf16x8 (&qf)[D / 16], f32x16 (&scur)[2], f32x16 (&snext)[2],
@@ -268,14 +359,11 @@ __device__ __forceinline__ void attend_step(const Tiles<D>& tl, const TileLoader
     const bool act_n = has_next && kv_nxt <= wave_last;
     const bool diag = kv_cur + kBN - 1 > q0;
     const int kv_2 = j + 2 < ntiles ? kv_of(j + 2) : 0;
-    if (j + 2 < ntiles) ld.load(krs, tl.k[PAR], kv_2);
-    if (has_next) ld.load(vrs, tl.v[1 - PAR], kv_nxt);
+    if (j + 2 < ntiles) ld.k.load(krs, tl.k[PAR], kv_2);
+    if (has_next) ld.v.load(vrs, tl.v[1 - PAR], kv_nxt);
     uint32_t pw[2][8];
     if (act && act_n && !diag) {
-        // steady state: one basic block so the scheduler can interleave the two MFMA streams with the VALU
-        softmax_tile<D>(scur, pw, st, c2, false, kv_cur, qrow, lane);
-        qk_tile<D>(tl.k[1 - PAR], qf, snext, lane);
-        pv_tile<D>(tl.v[PAR], va, pw, st);
+        steady_tile<D>(tl.k[1 - PAR], tl.v[PAR], va, qf, scur, snext, pw, st, c2, qrow, lane);
     } else {
         if (act) softmax_tile<D>(scur, pw, st, c2, diag, kv_cur, qrow, lane);
         if (act_n) qk_tile<D>(tl.k[1 - PAR], qf, snext, lane);
@@ -291,15 +379,15 @@ template <int D, int NW, typename KvOf>
 __device__ __forceinline__ void attend(const Tiles<D>& tl, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                        int ntiles, KvOf kv_of, const bf16x8 (&qf)[D / 16], RowState<D>& st, float c2,
                                        int q0, int wave_last, int w, int lane) {
-    TileLoader<D, NW> ld;
+    Loaders<D, NW> ld;
     ld.init(w, lane);
     VtAddr<D> va;
     va.init(lane);
     int kv_cur = kv_of(0);
     int kv_nxt = ntiles > 1 ? kv_of(1) : 0;
-    ld.load(krs, tl.k[0], kv_cur);
-    ld.load(vrs, tl.v[0], kv_cur);
-    if (ntiles > 1) ld.load(krs, tl.k[1], kv_nxt);
+    ld.k.load(krs, tl.k[0], kv_cur);
+    ld.v.load(vrs, tl.v[0], kv_cur);
+    if (ntiles > 1) ld.k.load(krs, tl.k[1], kv_nxt);
     wait_vmem();
     __syncthreads();
     f32x16 sa[2], sb[2];
@@ -336,10 +424,10 @@ struct DenseArgs {
 // head cycles fastest so that, with 8 XCDs dispatched round-robin, an XCD keeps seeing the same kv heads.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void prefill_dense_bf16_kernel(const DenseArgs a) {
-    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::TILE];
-    __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::TILE];
-    __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::TILE];
-    __shared__ __attribute__((aligned(1024))) char v1[Lds<D>::TILE];
+    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::KTILE];
+    __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::KTILE];
+    __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::VTILE];
+    __shared__ __attribute__((aligned(1024))) char v1[Lds<D>::VTILE];
     const Tiles<D> tl{{(lds_char*)k0, (lds_char*)k1}, {(lds_char*)v0, (lds_char*)v1}};
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int per_tile = a.B * a.Hkv * a.NHG;
@@ -370,6 +458,153 @@ __global__ __launch_bounds__(NW * 64) void prefill_dense_bf16_kernel(const Dense
     finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
 }
 
+// Ping-pong schedule for 8-wave work-groups. Waves w and w + 4 run on the same SIMD; the two groups (waves 0-3 and
+// 4-7) take opposite phases, so while one wave of a SIMD turns scores into probabilities on the VALU, the other
+// keeps the matrix cores busy, and they swap at the next barrier. Every wave runs the same program:
+//   QK(tile 0), then for each tile t: softmax(t) | PV(t) + QK(t+1),
+// with a work-group barrier between phases; group 1 enters one barrier late and group 0 leaves one barrier late,
+// so group 1 always runs one phase behind group 0. Pair t = (K of tile t+1, V of tile t) lives in buffer t % 2 and
+// is used by group 0 in global step 2t+2 and by group 1 in step 2t+3; pair t+1 is issued at the start of step 2t+2
+// (group 0 as it starts PV(t), group 1 as it starts softmax(t)) into the buffer pair t-1 left, and every wave waits
+// for its share at the end of step 2t+3, so each pair has two phases to land. K of tile 0 sits in buffer 1 first.
+
+// MFMA phase, hand-scheduled: the PV MFMAs of the held probabilities then the QK MFMAs of the next tile as one stream
+// of steps separated by hard scheduling barriers; step m issues the operand reads of MFMA m+2, then MFMA m.
+template <int D>
+__device__ __forceinline__ void mfma_phase(const lds_char* vl, const lds_char* kl, const VtAddr<D>& va,
+                                           const uint32_t (&pw)[2][8], const bf16x8 (&qf)[D / 16], f32x16 (&s)[2],
+                                           RowState<D>& st, int lane) {
+    constexpr int NPV = D / 8, NQK = D / 8, AH = 2;
+    const int hi = lane >> 5, ln = lane & 31;
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    bf16x8 kf[NQK];
+    v4i16 vlo[NPV], vhi[NPV];
+    auto reads = [&](int m) {
+        if (m < NPV) {
+            const int t = m / (2 * (D / 32)), u = (m / (D / 32)) & 1, dt = m % (D / 32);
+            const int key = 32 * t + 16 * u + va.key_lo, d = 32 * dt + va.dq;
+            vlo[m] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + va.at(key, d)));
+            vhi[m] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + va.at(key + 8, d)));
+        } else if (m < NPV + NQK) {
+            const int i = m - NPV, ks = i >> 1, r = 32 * (i & 1) + ln;
+            kf[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kl + r * Lds<D>::KSTR +
+                                                                                       (2 * ks + hi) * 16);
+        }
+    };
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int m = 0; m < AH; ++m) reads(m);
+#pragma unroll
+    for (int m = 0; m < NPV + NQK; ++m) {
+        reads(m + AH);
+        if (m < NPV) {
+            const int t = m / (2 * (D / 32)), u = (m / (D / 32)) & 1, dt = m % (D / 32);
+            const bf16x8 b = __builtin_bit_cast(
+                bf16x8, (u32x4{pw[t][4 * u], pw[t][4 * u + 1], pw[t][4 * u + 2], pw[t][4 * u + 3]}));
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, (u32x4{__builtin_bit_cast(u32x2, vlo[m])[0], __builtin_bit_cast(u32x2, vlo[m])[1],
+                               __builtin_bit_cast(u32x2, vhi[m])[0], __builtin_bit_cast(u32x2, vhi[m])[1]}));
+            st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, st.o[dt], 0, 0, 0);
+        } else {
+            const int i = m - NPV;
+            s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], s[i & 1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// One tile t of the ping-pong loop, buffer parity P = t % 2.
+template <int D, int P, typename KvOf, typename Act>
+__device__ __forceinline__ void pp_tile(const Tiles<D>& tl, const Loaders<D, 8>& ld, __amdgpu_buffer_rsrc_t krs,
+                                        __amdgpu_buffer_rsrc_t vrs, const VtAddr<D>& va, int t, int n, KvOf kv_of,
+                                        Act act, int grp, const bf16x8 (&qf)[D / 16], f32x16 (&s)[2],
+                                        uint32_t (&pw)[2][8], RowState<D>& st, float c2, int q0, int lane) {
+    auto issue_next = [&]() {   // pair t+1 into buffer 1-P
+        if (t + 1 < n) ld.v.load(vrs, tl.v[1 - P], kv_of(t + 1));
+        if (t + 2 < n) ld.k.load(krs, tl.k[1 - P], kv_of(t + 2));
+    };
+    __syncthreads();
+    if (grp == 1) issue_next();
+    if (act(t)) softmax_tile<D>(s, pw, st, c2, kv_of(t) + kBN - 1 > q0, kv_of(t), q0 + (lane & 31), lane);
+    if (grp == 0) wait_vmem();   // pair t
+    __syncthreads();
+    if (grp == 0) issue_next();
+    const bool pv = act(t), qk = act(t + 1);
+    if (pv && qk) {
+        mfma_phase<D>(tl.v[P], tl.k[P], va, pw, qf, s, st, lane);
+    } else {
+        if (pv) pv_tile<D>(tl.v[P], va, pw, st);
+        if (qk) qk_tile<D>(tl.k[P], qf, s, lane);
+    }
+    if (grp == 1) wait_vmem();   // pair t+1
+}
+
+template <int D, typename KvOf>
+__device__ __forceinline__ void attend_pp(const Tiles<D>& tl, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                          int n, KvOf kv_of, const bf16x8 (&qf)[D / 16], RowState<D>& st, float c2,
+                                          int q0, int wave_last, int w, int lane) {
+    Loaders<D, 8> ld;
+    ld.init(w, lane);
+    VtAddr<D> va;
+    va.init(lane);
+    const int grp = w >> 2;
+    auto act = [&](int t) { return t < n && kv_of(t) <= wave_last; };
+    ld.k.load(krs, tl.k[1], kv_of(0));
+    if (n > 1) ld.k.load(krs, tl.k[0], kv_of(1));
+    ld.v.load(vrs, tl.v[0], kv_of(0));
+    wait_vmem();
+    __syncthreads();
+    if (grp == 1) __syncthreads();
+    f32x16 s[2];
+    uint32_t pw[2][8];
+    if (act(0)) qk_tile<D>(tl.k[1], qf, s, lane);
+    int t = 0;
+    for (; t + 1 < n; t += 2) {
+        pp_tile<D, 0>(tl, ld, krs, vrs, va, t, n, kv_of, act, grp, qf, s, pw, st, c2, q0, lane);
+        pp_tile<D, 1>(tl, ld, krs, vrs, va, t + 1, n, kv_of, act, grp, qf, s, pw, st, c2, q0, lane);
+    }
+    if (t < n) pp_tile<D, 0>(tl, ld, krs, vrs, va, t, n, kv_of, act, grp, qf, s, pw, st, c2, q0, lane);
+    if (grp == 0) __syncthreads();
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void prefill_dense_pp_kernel(const DenseArgs a) {
+    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::KTILE];
+    __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::KTILE];
+    __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::VTILE];
+    __shared__ __attribute__((aligned(1024))) char v1[Lds<D>::VTILE];
+    const Tiles<D> tl{{(lds_char*)k0, (lds_char*)k1}, {(lds_char*)v0, (lds_char*)v1}};
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int per_tile = a.B * a.Hkv * a.NHG;
+    const int pt = a.n_ptiles - 1 - (int)(blockIdx.x / per_tile);
+    int rest = (int)(blockIdx.x % per_tile);
+    const int g = rest % a.Hkv;
+    rest /= a.Hkv;
+    const int hg = rest % a.NHG;
+    const int b = rest / a.NHG;
+    const int h = g * a.G + hg * a.HPW + (w % a.HPW);
+    const int p0 = pt * a.PPW;
+    const int q0 = p0 + 32 * (w / a.HPW);
+    const int wg_end = min(a.N, p0 + a.PPW);
+    const int ntiles = (wg_end + kBN - 1) / kBN;
+    const int qrow = q0 + (lane & 31);
+
+    const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)a.N * D;
+    const size_t kvoff = ((size_t)b * a.Hkv + g) * (size_t)a.N * D;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + kvoff, a.N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v + kvoff, a.N * D * 2);
+
+    bf16x8 qf[D / 16];
+    load_q<D>(qf, a.q + qoff, qrow, a.N, lane);
+    RowState<D> st;
+    init_state<D>(st);
+    const int wave_last = q0 < a.N ? min(q0 + 31, a.N - 1) : -1;
+    attend_pp<D>(tl, krs, vrs, ntiles, [](int t) { return t * kBN; }, qf, st, a.c2, q0, wave_last, w, lane);
+    finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
+}
+
 struct SparseArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -388,10 +623,10 @@ struct SparseArgs {
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_sparse_bf16_kernel(const SparseArgs a) {
-    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::TILE];
-    __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::TILE];
-    __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::TILE];
-    __shared__ __attribute__((aligned(1024))) char v1[Lds<D>::TILE];
+    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::KTILE];
+    __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::KTILE];
+    __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::VTILE];
+    __shared__ __attribute__((aligned(1024))) char v1[Lds<D>::VTILE];
     const Tiles<D> tl{{(lds_char*)k0, (lds_char*)k1}, {(lds_char*)v0, (lds_char*)v1}};
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int per = a.B * a.Hq;
@@ -420,7 +655,7 @@ void prefill_sparse_bf16_kernel(const SparseArgs a) {
     if (ntiles == 0) return;  // every valid list holds the diagonal; an empty one leaves the rows unwritten
     // the row's block list goes to LDS once, so the tile loop reads the next tile's block in LDS latency instead
     // of a global round trip per tile
-    __shared__ int lst[kMaxBlocks];
+    extern __shared__ int lst[];   // nb entries, sized at launch
     for (int e = tid; e < cnt; e += NW * 64) lst[e] = list[e];
     __syncthreads();
     const int blk = a.block;
@@ -533,9 +768,9 @@ hipError_t launch_prefill_dense_bf16(const PrefillProblem& p, hipStream_t s) {
     a.c2 = p.scale * kLog2e;
     const dim3 grid((unsigned)(a.n_ptiles * a.B * a.Hkv * a.NHG));
     if (p.D == 128)
-        hipLaunchKernelGGL((prefill_dense_bf16_kernel<128, NW>), grid, dim3(NW * 64), 0, s, a);
+        hipLaunchKernelGGL((prefill_dense_pp_kernel<128>), grid, dim3(NW * 64), 0, s, a);
     else
-        hipLaunchKernelGGL((prefill_dense_bf16_kernel<64, NW>), grid, dim3(NW * 64), 0, s, a);
+        hipLaunchKernelGGL((prefill_dense_pp_kernel<64>), grid, dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 
@@ -558,16 +793,17 @@ hipError_t launch_prefill_sparse_bf16(const PrefillProblem& p, int block, const 
     a.nb = p.N / block;
     a.c2 = p.scale * kLog2e;
     const dim3 grid((unsigned)(a.nb * a.B * a.Hq));
+    const size_t lst_bytes = ((size_t)a.nb * sizeof(int32_t) + 15) / 16 * 16;   // the kept-block list in LDS
     // one wave per 32 rows of the query block
     if (block == 64) {
-        if (p.D == 128) hipLaunchKernelGGL((prefill_sparse_bf16_kernel<128, 2>), grid, dim3(128), 0, s, a);
-        else hipLaunchKernelGGL((prefill_sparse_bf16_kernel<64, 2>), grid, dim3(128), 0, s, a);
+        if (p.D == 128) hipLaunchKernelGGL((prefill_sparse_bf16_kernel<128, 2>), grid, dim3(128), lst_bytes, s, a);
+        else hipLaunchKernelGGL((prefill_sparse_bf16_kernel<64, 2>), grid, dim3(128), lst_bytes, s, a);
     } else if (block == 128) {
-        if (p.D == 128) hipLaunchKernelGGL((prefill_sparse_bf16_kernel<128, 4>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((prefill_sparse_bf16_kernel<64, 4>), grid, dim3(256), 0, s, a);
+        if (p.D == 128) hipLaunchKernelGGL((prefill_sparse_bf16_kernel<128, 4>), grid, dim3(256), lst_bytes, s, a);
+        else hipLaunchKernelGGL((prefill_sparse_bf16_kernel<64, 4>), grid, dim3(256), lst_bytes, s, a);
     } else if (block == 256) {
-        if (p.D == 128) hipLaunchKernelGGL((prefill_sparse_bf16_kernel<128, 8>), grid, dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((prefill_sparse_bf16_kernel<64, 8>), grid, dim3(512), 0, s, a);
+        if (p.D == 128) hipLaunchKernelGGL((prefill_sparse_bf16_kernel<128, 8>), grid, dim3(512), lst_bytes, s, a);
+        else hipLaunchKernelGGL((prefill_sparse_bf16_kernel<64, 8>), grid, dim3(512), lst_bytes, s, a);
     } else {
         return hipErrorInvalidValue;
     }
