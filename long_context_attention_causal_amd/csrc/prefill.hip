@@ -419,45 +419,6 @@ struct DenseArgs {
     float c2;      // scale * log2(e)
 };
 
-// Work-group = HPW query heads of one kv group x PPW consecutive positions; waves = heads x 32-row slices.
-// All waves share each staged K/V tile. Work-groups are issued heaviest (latest positions) first, and the kv
-// head cycles fastest so that, with 8 XCDs dispatched round-robin, an XCD keeps seeing the same kv heads.
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void prefill_dense_bf16_kernel(const DenseArgs a) {
-    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::KTILE];
-    __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::KTILE];
-    __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::VTILE];
-    __shared__ __attribute__((aligned(1024))) char v1[Lds<D>::VTILE];
-    const Tiles<D> tl{{(lds_char*)k0, (lds_char*)k1}, {(lds_char*)v0, (lds_char*)v1}};
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int per_tile = a.B * a.Hkv * a.NHG;
-    const int pt = a.n_ptiles - 1 - (int)(blockIdx.x / per_tile);
-    int rest = (int)(blockIdx.x % per_tile);
-    const int g = rest % a.Hkv;
-    rest /= a.Hkv;
-    const int hg = rest % a.NHG;
-    const int b = rest / a.NHG;
-    const int h = g * a.G + hg * a.HPW + (w % a.HPW);
-    const int p0 = pt * a.PPW;
-    const int q0 = p0 + 32 * (w / a.HPW);
-    const int wg_end = min(a.N, p0 + a.PPW);
-    const int ntiles = (wg_end + kBN - 1) / kBN;
-    const int qrow = q0 + (lane & 31);
-
-    const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)a.N * D;
-    const size_t kvoff = ((size_t)b * a.Hkv + g) * (size_t)a.N * D;
-    const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + kvoff, a.N * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v + kvoff, a.N * D * 2);
-
-    bf16x8 qf[D / 16];
-    load_q<D>(qf, a.q + qoff, qrow, a.N, lane);
-    RowState<D> st;
-    init_state<D>(st);
-    const int wave_last = q0 < a.N ? min(q0 + 31, a.N - 1) : -1;
-    attend<D, NW>(tl, krs, vrs, ntiles, [](int t) { return t * kBN; }, qf, st, a.c2, q0, wave_last, w, lane);
-    finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
-}
-
 // Ping-pong schedule for 8-wave work-groups. Waves w and w + 4 run on the same SIMD; the two groups (waves 0-3 and
 // 4-7) take opposite phases, so while one wave of a SIMD turns scores into probabilities on the VALU, the other
 // keeps the matrix cores busy, and they swap at the next barrier. Every wave runs the same program:
@@ -568,6 +529,9 @@ __device__ __forceinline__ void attend_pp(const Tiles<D>& tl, __amdgpu_buffer_rs
     if (grp == 0) __syncthreads();
 }
 
+// Work-group = HPW query heads of one kv group x PPW consecutive positions; waves = heads x 32-row slices.
+// All waves share each staged K/V tile. Work-groups are issued heaviest (latest positions) first, and the kv
+// head cycles fastest so that, with 8 XCDs dispatched round-robin, an XCD keeps seeing the same kv heads.
 template <int D>
 __global__ __launch_bounds__(512) void prefill_dense_pp_kernel(const DenseArgs a) {
     __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::KTILE];
@@ -631,7 +595,10 @@ void prefill_sparse_bf16_kernel(const SparseArgs a) {
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int per = a.B * a.Hq;
     const int i = a.nb - 1 - (int)(blockIdx.x / per);
-    const int rest = (int)(blockIdx.x % per);
+    int rest = (int)(blockIdx.x % per);
+    // work-groups go to the 8 XCDs round-robin; when the heads split evenly, XCD x takes the x-th run of per / 8
+    // heads in kv-group order, so its L2 serves as few kv heads as possible
+    if (per % 8 == 0) rest = (rest % 8) * (per / 8) + rest / 8;
     const int h = rest % a.Hq;
     const int b = rest / a.Hq;
     const int g = h / a.G;
