@@ -65,6 +65,8 @@ def test_fp32_ragged(lib, B, Hq, Hkv, N, D):
     (1, 4, 4, 1, 128),       # a single token
     (1, 8, 8, 64, 64),       # exactly one tile
     (1, 16, 2, 1000, 128),   # G = 8 with several position tiles
+    (1, 16, 1, 500, 128),    # G = 16: two work-groups per position block
+    (2, 8, 1, 700, 64),      # head_dim 64, G = 8, two sequences
 ])
 def test_bf16_small(lib, B, Hq, Hkv, N, D):
     check_full(lib, W.dense_inputs(21, B, Hq, Hkv, N, D, "bf16"), BF16_TOL, LSE_TOL, f"bf16 {B},{Hq},{Hkv},{N},{D}")

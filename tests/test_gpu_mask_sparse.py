@@ -114,21 +114,24 @@ def run_sparse(lib, inp, kv_count, kv_index):
     return o, lse
 
 
-@pytest.mark.parametrize("Hq,Hkv,N,D,block,keep,alpha", [
-    (8, 2, 64 * 20, 128, 64, 150, 1.0),
-    (4, 1, 128 * 12, 128, 128, 100, 1.0),
-    (8, 4, 64 * 11, 64, 64, 200, 0.5),
-    (4, 2, 256 * 6, 128, 256, 300, 1.0),
-    (8, 2, 64 * 20, 128, 64, 0, math.inf),     # diagonal blocks only
+@pytest.mark.parametrize("B,Hq,Hkv,N,D,block,keep,alpha", [
+    (1, 8, 2, 64 * 20, 128, 64, 150, 1.0),
+    (1, 4, 1, 128 * 12, 128, 128, 100, 1.0),
+    (1, 8, 4, 64 * 11, 64, 64, 200, 0.5),
+    (1, 4, 2, 256 * 6, 128, 256, 300, 1.0),
+    (1, 8, 2, 64 * 20, 128, 64, 0, math.inf),  # diagonal blocks only
+    (2, 8, 2, 64 * 12, 128, 64, 150, 1.0),     # two sequences: the head order spans the batch
+    (1, 24, 3, 128 * 6, 128, 128, 100, 1.0),   # 24 heads: three per XCD in kv-group order
+    (1, 16, 1, 64 * 10, 64, 64, 200, 1.0),     # G = 16, head_dim 64
 ])
-def test_sparse_small_full(lib, Hq, Hkv, N, D, block, keep, alpha):
-    inp = W.planted_inputs(43, 1, Hq, Hkv, N, D, block)
+def test_sparse_small_full(lib, B, Hq, Hkv, N, D, block, keep, alpha):
+    inp = W.planted_inputs(43, B, Hq, Hkv, N, D, block)
     q, k, v = inp.as_f64()
     ref = M.build_mask(q, k, inp.scale, block, keep, alpha)
     o, lse = run_sparse(lib, inp, ref.kv_count, ref.kv_index)
     Oref, Lref = A.masked_attention(q, k, v, inp.scale, ref.mask, block)
     eo, el = max_err(host64(o), Oref), max_err(host64(lse), Lref)
-    say(f"[sparse] small {Hq},{Hkv},{N},{D},b{block} max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    say(f"[sparse] small {B},{Hq},{Hkv},{N},{D},b{block} max|dO|={eo:.3e} max|dlse|={el:.3e}")
     assert eo <= BF16_TOL and el <= LSE_TOL
 
 
