@@ -5,15 +5,16 @@
 // "Inference-specific: Flash-Decoding and FlashInfer"); the KV cache is a pool of fixed-size pages placed
 // anywhere and found through a per-sequence block table (same page, section "PagedAttention").
 //
-// Split kernel: work-group = (chunk of chunk_tokens tokens, kv head, sequence), 4 waves, each wave a quarter of
-// the chunk's pages. Every (page, kv head) is one contiguous slab of 16 x head_dim bf16, so the K slab is read
-// straight into the A operand of v_mfma_f32_16x16x32_bf16 (lane = token row, 16-byte pieces of the head dim)
-// and S^T = K Q^T comes out with the group's query heads as columns. All page loads of a wave are issued
-// before any is used, to keep many bytes in flight. V is written transposed into LDS (zero for slots past the
-// sequence end, so NaN padding cannot leak) and read back as the A operand of v_mfma_f32_16x16x16_bf16 with the
-// bf16 probabilities as B, which are already in B-operand order in the lane that computed them.
-// The four wave partials are merged in LDS; the chunk's normalised output and natural-log lse go to the
-// workspace. Combine kernel: one wave per (sequence, query head) merges the chunks by log-sum-exp.
+// Split kernel: work-group = (chunk of chunk_tokens tokens, kv head, sequence), 1, 2 or 4 waves, each streaming its
+// share of the chunk's pages in batches of 2 or 4 pages with the next batch in flight. Every (page, kv head) is
+// one contiguous slab of 16 x head_dim bf16, so the K slab is read straight into the A operand of
+// v_mfma_f32_16x16x32_bf16 (lane = token row, 16-byte pieces of the head dim) and S^T = K Q^T comes out with the
+// group's query heads as columns. V goes from HBM straight into LDS in its natural layout and comes back as the A
+// operand of v_mfma_f32_16x16x16_bf16 through ds_read_b64_tr_b16, with the bf16 probabilities as B, which are
+// already in B-operand order in the lane that computed them. Each page's buffer view ends at the sequence end,
+// so slots past it read as zeros and NaN padding cannot leak.
+// The wave partials are merged in LDS; the chunk's normalised output and natural-log lse go to the workspace.
+// Combine kernel: one wave per (sequence, query head) merges the chunks by log-sum-exp.
 #include "device_common.hpp"
 #include "internal.hpp"
 

@@ -8,18 +8,22 @@
 //
 // bf16 tile body (one wave = 32 query rows of one head, one KV tile = 64 keys):
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = the wave's Q rows held in VGPRs for
-//   the whole kernel. In the 32x32 accumulator layout lane l owns query column l%32 and 16 keys, so a row
+//   the whole work-group. In the 32x32 accumulator layout lane l owns query column l%32 and 16 keys, so a row
 //   max/sum is 15 in-lane ops plus one exchange with lane l^32.
 //   O^T += V^T P^T with the same MFMA: the bf16-rounded probabilities are already in B-operand order in the
-//   lane that computed them (no LDS round trip); V is stored transposed in LDS when it is staged, with the
-//   key order inside each 16-key group permuted so every A operand is one 16-byte LDS read.
+//   lane that computed them (no LDS round trip); V stays in its natural row-major layout in LDS and each A
+//   operand is two ds_read_b64_tr_b16 reads, which transpose 4 keys x 16 head dims per 16-lane group.
 //   The running max is refreshed lazily: only when a tile's max exceeds it by more than 2^8, which keeps
 //   every exp2 argument <= 8 and skips the O rescale on almost every tile. The final normalisation uses the
 //   same max, so the result is unchanged up to rounding.
 //   The row sum adds the bf16-rounded probabilities (v_dot2_f32_bf16), i.e. exactly the weights the PV
 //   product uses.
-// Staging: K/V tiles for step j+1 are fetched into VGPRs while step j computes, then written to the other of
-// two LDS buffers; one barrier per step.
+// Staging: K and V tiles go from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane, no staging
+// registers) into one of two buffers while the other is in use.
+// Schedules: the dense kernel is an 8-wave ping-pong (waves w and w+4 share a SIMD and alternate between the
+// softmax on the VALU and the MFMA stream, one work-group barrier per phase); the block-sparse kernel runs one
+// phase per tile in each wave (the next tile's QK MFMAs interleaved with this tile's softmax, then this tile's PV).
+// The file is compiled without NaN semantics (see the build script): a max then needs no quieting of its inputs.
 #include "device_common.hpp"
 #include "internal.hpp"
 
