@@ -573,6 +573,40 @@ __global__ __launch_bounds__(512) void prefill_dense_pp_kernel(const DenseArgs a
     finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
 }
 
+// Single-buffered tile walk for small work-groups: one K and one V tile in LDS. The next K tile is requested as soon
+// as every wave has finished this tile's QK product (it lands during the softmax and PV), the next V tile once PV is
+// done. With half the LDS of the double-buffered walk, twice as many work-groups share a CU (two waves per SIMD
+// instead of one for 64-row blocks) and cover each other's load latency.
+template <int D, int NW, typename KvOf>
+__device__ __forceinline__ void attend_sb(const lds_char* kl, const lds_char* vl, __amdgpu_buffer_rsrc_t krs,
+                                          __amdgpu_buffer_rsrc_t vrs, int ntiles, KvOf kv_of,
+                                          const bf16x8 (&qf)[D / 16], RowState<D>& st, float c2, int q0, int w,
+                                          int lane) {
+    Loaders<D, NW> ld;
+    ld.init(w, lane);
+    VtAddr<D> va;
+    va.init(lane);
+    const int qrow = q0 + (lane & 31);
+    int kv = kv_of(0);
+    ld.k.load(krs, (lds_char*)kl, kv);
+    ld.v.load(vrs, (lds_char*)vl, kv);
+    for (int j = 0; j < ntiles; ++j) {
+        const int kv_n = j + 1 < ntiles ? kv_of(j + 1) : 0;
+        wait_vmem();
+        __syncthreads();
+        f32x16 s[2];
+        uint32_t pw[2][8];
+        qk_tile<D>(kl, qf, s, lane);
+        __syncthreads();   // every wave is done with K(j)
+        if (j + 1 < ntiles) ld.k.load(krs, (lds_char*)kl, kv_n);
+        softmax_tile<D>(s, pw, st, c2, kv + kBN - 1 > q0, kv, qrow, lane);
+        pv_tile<D>(vl, va, pw, st);
+        __syncthreads();   // and with V(j)
+        if (j + 1 < ntiles) ld.v.load(vrs, (lds_char*)vl, kv_n);
+        kv = kv_n;
+    }
+}
+
 struct SparseArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -587,7 +621,9 @@ struct SparseArgs {
 
 // Work-group = one (batch, head, query block); NW = block / 32 waves. The tile loop walks the row's kept-block
 // list (ascending, so the diagonal block, the only one needing an element mask, comes last); skipped blocks
-// are never read. Rows are issued latest block first, as they tend to hold the longest lists.
+// are never read. Rows are issued latest block first, as they tend to hold the longest lists. Two-wave work-groups
+// (64-row blocks) walk with one buffer per tile (their register budget allows two waves per SIMD once LDS does),
+// larger ones with the double-buffered one-phase step.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_sparse_bf16_kernel(const SparseArgs a) {
@@ -630,8 +666,12 @@ void prefill_sparse_bf16_kernel(const SparseArgs a) {
     for (int e = tid; e < cnt; e += NW * 64) lst[e] = list[e];
     __syncthreads();
     const int blk = a.block;
-    attend<D, NW>(tl, krs, vrs, ntiles, [&](int t) { return lst[t / sub] * blk + (t % sub) * kBN; }, qf, st, a.c2,
-                  q0, q0 + 31, w, lane);
+    if constexpr (NW == 2)
+        attend_sb<D, NW>(tl.k[0], tl.v[0], krs, vrs, ntiles, [&](int t) { return lst[t / sub] * blk + (t % sub) * kBN; },
+                         qf, st, a.c2, q0, w, lane);
+    else
+        attend<D, NW>(tl, krs, vrs, ntiles, [&](int t) { return lst[t / sub] * blk + (t % sub) * kBN; }, qf, st, a.c2,
+                      q0, q0 + 31, w, lane);
     finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
 }
 
