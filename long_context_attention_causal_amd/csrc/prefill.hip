@@ -621,11 +621,12 @@ struct SparseArgs {
 
 // Work-group = one (batch, head, query block); NW = block / 32 waves. The tile loop walks the row's kept-block
 // list (ascending, so the diagonal block, the only one needing an element mask, comes last); skipped blocks
-// are never read. Rows are issued latest block first, as they tend to hold the longest lists. Two-wave work-groups
-// (64-row blocks) walk with one buffer per tile (their register budget allows two waves per SIMD once LDS does),
-// larger ones with the double-buffered one-phase step.
+// are never read. Rows are issued latest block first, as they tend to hold the longest lists. Work-groups of two
+// and four waves (64- and 128-row blocks) walk with one buffer per tile: the LDS saved lets 4 and 3 work-groups
+// share a CU (two and three waves per SIMD; the four-wave kernel is held to the register budget of three).
+// Eight-wave work-groups keep the double-buffered one-phase step.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 3 : 2)))
 void prefill_sparse_bf16_kernel(const SparseArgs a) {
     __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::KTILE];
     __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::KTILE];
@@ -666,7 +667,7 @@ void prefill_sparse_bf16_kernel(const SparseArgs a) {
     for (int e = tid; e < cnt; e += NW * 64) lst[e] = list[e];
     __syncthreads();
     const int blk = a.block;
-    if constexpr (NW == 2)
+    if constexpr (NW <= 4)
         attend_sb<D, NW>(tl.k[0], tl.v[0], krs, vrs, ntiles, [&](int t) { return lst[t / sub] * blk + (t % sub) * kBN; },
                          qf, st, a.c2, q0, w, lane);
     else
