@@ -265,7 +265,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": tflops2, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops2 / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic("prefill_dense_c2", "prefill.hip"),
-                     "kernel": "prefill_dense_pp_kernel<128>", "per_launch_flop": fl2,
+                     "kernel": "prefill_dense_kernel<128>", "per_launch_flop": fl2,
                      "algorithmic_bytes": float((B * Hq + 2 * c2.k.shape[1]) * N * D * 2 + B * Hq * N * D * 2)},
         "cpu_baseline": cpu,
         "paths": paths,

@@ -20,9 +20,10 @@
 //   product uses.
 // Staging: K and V tiles go from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane, no staging
 // registers) into one of two buffers while the other is in use.
-// Schedules: the dense kernel is an 8-wave ping-pong (waves w and w+4 share a SIMD and alternate between the
-// softmax on the VALU and the MFMA stream, one work-group barrier per phase); the block-sparse kernel runs one
-// phase per tile in each wave (the next tile's QK MFMAs interleaved with this tile's softmax, then this tile's PV).
+// Schedules: dense work-groups and block-sparse ones of up to 128 rows walk their tiles single-buffered (QK, softmax,
+// PV per tile; the next K tile requested once every wave is done with the current one), small enough in LDS and
+// registers that several work-groups share each CU and overlap each other; 256-row block-sparse work-groups run one
+// double-buffered phase per tile in each wave (the next tile's QK MFMAs interleaved with this tile's softmax).
 // The file is compiled without NaN semantics (see the build script): a max then needs no quieting of its inputs.
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -31,6 +32,7 @@ namespace lcattn {
 namespace {
 
 constexpr int kBN = 64;        // keys per KV tile
+constexpr int kDenseWaves = 4; // waves per dense work-group
 constexpr float kSlack = 8.0f; // lazy-rescale threshold, log2 units
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -423,155 +425,6 @@ struct DenseArgs {
     float c2;      // scale * log2(e)
 };
 
-// Ping-pong schedule for 8-wave work-groups. Waves w and w + 4 run on the same SIMD; the two groups (waves 0-3 and
-// 4-7) take opposite phases, so while one wave of a SIMD turns scores into probabilities on the VALU, the other
-// keeps the matrix cores busy, and they swap at the next barrier. Every wave runs the same program:
-//   QK(tile 0), then for each tile t: softmax(t) | PV(t) + QK(t+1),
-// with a work-group barrier between phases; group 1 enters one barrier late and group 0 leaves one barrier late,
-// so group 1 always runs one phase behind group 0. Pair t = (K of tile t+1, V of tile t) lives in buffer t % 2 and
-// is used by group 0 in global step 2t+2 and by group 1 in step 2t+3; pair t+1 is issued at the start of step 2t+2
-// (group 0 as it starts PV(t), group 1 as it starts softmax(t)) into the buffer pair t-1 left, and every wave waits
-// for its share at the end of step 2t+3, so each pair has two phases to land. K of tile 0 sits in buffer 1 first.
-
-// MFMA phase, hand-scheduled: the PV MFMAs of the held probabilities then the QK MFMAs of the next tile as one stream
-// of steps separated by hard scheduling barriers; step m issues the operand reads of MFMA m+2, then MFMA m.
-template <int D>
-__device__ __forceinline__ void mfma_phase(const lds_char* vl, const lds_char* kl, const VtAddr<D>& va,
-                                           const uint32_t (&pw)[2][8], const bf16x8 (&qf)[D / 16], f32x16 (&s)[2],
-                                           RowState<D>& st, int lane) {
-    constexpr int NPV = D / 8, NQK = D / 8, AH = 2;
-    const int hi = lane >> 5, ln = lane & 31;
-    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-    bf16x8 kf[NQK];
-    v4i16 vlo[NPV], vhi[NPV];
-    auto reads = [&](int m) {
-        if (m < NPV) {
-            const int t = m / (2 * (D / 32)), u = (m / (D / 32)) & 1, dt = m % (D / 32);
-            const int key = 32 * t + 16 * u + va.key_lo, d = 32 * dt + va.dq;
-            vlo[m] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + va.at(key, d)));
-            vhi[m] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + va.at(key + 8, d)));
-        } else if (m < NPV + NQK) {
-            const int i = m - NPV, ks = i >> 1, r = 32 * (i & 1) + ln;
-            kf[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kl + r * Lds<D>::KSTR +
-                                                                                       (2 * ks + hi) * 16);
-        }
-    };
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-#pragma unroll
-    for (int m = 0; m < AH; ++m) reads(m);
-#pragma unroll
-    for (int m = 0; m < NPV + NQK; ++m) {
-        reads(m + AH);
-        if (m < NPV) {
-            const int t = m / (2 * (D / 32)), u = (m / (D / 32)) & 1, dt = m % (D / 32);
-            const bf16x8 b = __builtin_bit_cast(
-                bf16x8, (u32x4{pw[t][4 * u], pw[t][4 * u + 1], pw[t][4 * u + 2], pw[t][4 * u + 3]}));
-            const bf16x8 a = __builtin_bit_cast(
-                bf16x8, (u32x4{__builtin_bit_cast(u32x2, vlo[m])[0], __builtin_bit_cast(u32x2, vlo[m])[1],
-                               __builtin_bit_cast(u32x2, vhi[m])[0], __builtin_bit_cast(u32x2, vhi[m])[1]}));
-            st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, st.o[dt], 0, 0, 0);
-        } else {
-            const int i = m - NPV;
-            s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], s[i & 1], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// One tile t of the ping-pong loop, buffer parity P = t % 2.
-template <int D, int P, typename KvOf, typename Act>
-__device__ __forceinline__ void pp_tile(const Tiles<D>& tl, const Loaders<D, 8>& ld, __amdgpu_buffer_rsrc_t krs,
-                                        __amdgpu_buffer_rsrc_t vrs, const VtAddr<D>& va, int t, int n, KvOf kv_of,
-                                        Act act, int grp, const bf16x8 (&qf)[D / 16], f32x16 (&s)[2],
-                                        uint32_t (&pw)[2][8], RowState<D>& st, float c2, int q0, int lane) {
-    auto issue_next = [&]() {   // pair t+1 into buffer 1-P
-        if (t + 1 < n) ld.v.load(vrs, tl.v[1 - P], kv_of(t + 1));
-        if (t + 2 < n) ld.k.load(krs, tl.k[1 - P], kv_of(t + 2));
-    };
-    __syncthreads();
-    if (grp == 1) issue_next();
-    if (act(t)) softmax_tile<D>(s, pw, st, c2, kv_of(t) + kBN - 1 > q0, kv_of(t), q0 + (lane & 31), lane);
-    if (grp == 0) wait_vmem();   // pair t
-    __syncthreads();
-    if (grp == 0) issue_next();
-    const bool pv = act(t), qk = act(t + 1);
-    if (pv && qk) {
-        mfma_phase<D>(tl.v[P], tl.k[P], va, pw, qf, s, st, lane);
-    } else {
-        if (pv) pv_tile<D>(tl.v[P], va, pw, st);
-        if (qk) qk_tile<D>(tl.k[P], qf, s, lane);
-    }
-    if (grp == 1) wait_vmem();   // pair t+1
-}
-
-template <int D, typename KvOf>
-__device__ __forceinline__ void attend_pp(const Tiles<D>& tl, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                          int n, KvOf kv_of, const bf16x8 (&qf)[D / 16], RowState<D>& st, float c2,
-                                          int q0, int wave_last, int w, int lane) {
-    Loaders<D, 8> ld;
-    ld.init(w, lane);
-    VtAddr<D> va;
-    va.init(lane);
-    const int grp = w >> 2;
-    auto act = [&](int t) { return t < n && kv_of(t) <= wave_last; };
-    ld.k.load(krs, tl.k[1], kv_of(0));
-    if (n > 1) ld.k.load(krs, tl.k[0], kv_of(1));
-    ld.v.load(vrs, tl.v[0], kv_of(0));
-    wait_vmem();
-    __syncthreads();
-    if (grp == 1) __syncthreads();
-    f32x16 s[2];
-    uint32_t pw[2][8];
-    if (act(0)) qk_tile<D>(tl.k[1], qf, s, lane);
-    int t = 0;
-    for (; t + 1 < n; t += 2) {
-        pp_tile<D, 0>(tl, ld, krs, vrs, va, t, n, kv_of, act, grp, qf, s, pw, st, c2, q0, lane);
-        pp_tile<D, 1>(tl, ld, krs, vrs, va, t + 1, n, kv_of, act, grp, qf, s, pw, st, c2, q0, lane);
-    }
-    if (t < n) pp_tile<D, 0>(tl, ld, krs, vrs, va, t, n, kv_of, act, grp, qf, s, pw, st, c2, q0, lane);
-    if (grp == 0) __syncthreads();
-}
-
-// Work-group = HPW query heads of one kv group x PPW consecutive positions; waves = heads x 32-row slices.
-// All waves share each staged K/V tile. Work-groups are issued heaviest (latest positions) first, and the kv
-// head cycles fastest so that, with 8 XCDs dispatched round-robin, an XCD keeps seeing the same kv heads.
-template <int D>
-__global__ __launch_bounds__(512) void prefill_dense_pp_kernel(const DenseArgs a) {
-    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::KTILE];
-    __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::KTILE];
-    __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::VTILE];
-    __shared__ __attribute__((aligned(1024))) char v1[Lds<D>::VTILE];
-    const Tiles<D> tl{{(lds_char*)k0, (lds_char*)k1}, {(lds_char*)v0, (lds_char*)v1}};
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int per_tile = a.B * a.Hkv * a.NHG;
-    const int pt = a.n_ptiles - 1 - (int)(blockIdx.x / per_tile);
-    int rest = (int)(blockIdx.x % per_tile);
-    const int g = rest % a.Hkv;
-    rest /= a.Hkv;
-    const int hg = rest % a.NHG;
-    const int b = rest / a.NHG;
-    const int h = g * a.G + hg * a.HPW + (w % a.HPW);
-    const int p0 = pt * a.PPW;
-    const int q0 = p0 + 32 * (w / a.HPW);
-    const int wg_end = min(a.N, p0 + a.PPW);
-    const int ntiles = (wg_end + kBN - 1) / kBN;
-    const int qrow = q0 + (lane & 31);
-
-    const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)a.N * D;
-    const size_t kvoff = ((size_t)b * a.Hkv + g) * (size_t)a.N * D;
-    const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + kvoff, a.N * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v + kvoff, a.N * D * 2);
-
-    bf16x8 qf[D / 16];
-    load_q<D>(qf, a.q + qoff, qrow, a.N, lane);
-    RowState<D> st;
-    init_state<D>(st);
-    const int wave_last = q0 < a.N ? min(q0 + 31, a.N - 1) : -1;
-    attend_pp<D>(tl, krs, vrs, ntiles, [](int t) { return t * kBN; }, qf, st, a.c2, q0, wave_last, w, lane);
-    finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
-}
 
 // Single-buffered tile walk for small work-groups: one K and one V tile in LDS. The next K tile is requested as soon
 // as every wave has finished this tile's QK product (it lands during the softmax and PV), the next V tile once PV is
@@ -605,6 +458,48 @@ __device__ __forceinline__ void attend_sb(const lds_char* kl, const lds_char* vl
         if (j + 1 < ntiles) ld.v.load(vrs, (lds_char*)vl, kv_n);
         kv = kv_n;
     }
+}
+
+// Dense kernel. Work-group = HPW query heads of one kv group x PPW consecutive positions, one wave per head and
+// 32-row slice (4 waves), all sharing each staged K/V tile; the single-buffered walk keeps a work-group at 38 KB of
+// LDS and the register budget is held to three waves per SIMD, so three work-groups share a CU and overlap each
+// other's loads, softmax and MFMA streams. Work-groups are issued heaviest (latest positions) first, and the kv head
+// cycles fastest so that, with 8 XCDs dispatched round-robin, an XCD keeps seeing the same kv heads.
+template <int D>
+__global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void prefill_dense_kernel(const DenseArgs a) {
+    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::KTILE];
+    __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::VTILE];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int per_tile = a.B * a.Hkv * a.NHG;
+    const int pt = a.n_ptiles - 1 - (int)(blockIdx.x / per_tile);
+    int rest = (int)(blockIdx.x % per_tile);
+    const int g = rest % a.Hkv;
+    rest /= a.Hkv;
+    const int hg = rest % a.NHG;
+    const int b = rest / a.NHG;
+    const int h = g * a.G + hg * a.HPW + (w % a.HPW);
+    const int p0 = pt * a.PPW;
+    const int q0 = p0 + 32 * (w / a.HPW);
+    const int wg_end = min(a.N, p0 + a.PPW);
+    const int ntiles = (wg_end + kBN - 1) / kBN;
+    const int qrow = q0 + (lane & 31);
+
+    const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)a.N * D;
+    const size_t kvoff = ((size_t)b * a.Hkv + g) * (size_t)a.N * D;
+    const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + kvoff, a.N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v + kvoff, a.N * D * 2);
+
+    bf16x8 qf[D / 16];
+    load_q<D>(qf, a.q + qoff, qrow, a.N, lane);
+    RowState<D> st;
+    init_state<D>(st);
+    // every wave walks the work-group's tiles; a tile wholly past a wave's rows (possible when one work-group spans
+    // several 32-row slices) is fully masked for it and adds nothing
+    attend_sb<D, kDenseWaves>((lds_char*)k0, (lds_char*)v0, krs, vrs, ntiles, [](int t) { return t * kBN; }, qf, st,
+                              a.c2, q0, w, lane);
+    finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
 }
 
 struct SparseArgs {
@@ -761,7 +656,7 @@ static int gcd_int(int x, int y) {
 }  // namespace
 
 hipError_t launch_prefill_dense_bf16(const PrefillProblem& p, hipStream_t s) {
-    constexpr int NW = 8;
+    constexpr int NW = kDenseWaves;
     DenseArgs a;
     a.q = static_cast<const uint16_t*>(p.q);
     a.k = static_cast<const uint16_t*>(p.k);
@@ -780,9 +675,9 @@ hipError_t launch_prefill_dense_bf16(const PrefillProblem& p, hipStream_t s) {
     a.c2 = p.scale * kLog2e;
     const dim3 grid((unsigned)(a.n_ptiles * a.B * a.Hkv * a.NHG));
     if (p.D == 128)
-        hipLaunchKernelGGL((prefill_dense_pp_kernel<128>), grid, dim3(NW * 64), 0, s, a);
+        hipLaunchKernelGGL((prefill_dense_kernel<128>), grid, dim3(NW * 64), 0, s, a);
     else
-        hipLaunchKernelGGL((prefill_dense_pp_kernel<64>), grid, dim3(NW * 64), 0, s, a);
+        hipLaunchKernelGGL((prefill_dense_kernel<64>), grid, dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 
