@@ -188,62 +188,93 @@ struct ScoreArgs {
     double scale;
 };
 
-// 64x64 output tile per work-group, 4x4 per thread, head dim in chunks of 16 through LDS.
+// 128 x 128 output tile per work-group (rows: the kv head's query heads stacked, hl * nb + i; columns: key blocks),
+// 8 x 8 per thread, the head dim in chunks of 8 through double-buffered LDS with the next chunk loaded into registers
+// while the current one is used. Thread (tr, tc) of a 16 x 16 grid owns rows 8 tr .. 8 tr + 7 and columns
+// 32 k + 2 tc + {0, 1}, k = 0..3 (so a 16-lane row of column reads is one contiguous 256-byte run). The head-dim sum
+// runs in order d = 0 .. D-1 with one fma per term, as before. Tiles wholly above the diagonal are skipped.
+constexpr int kST = 128;    // tile edge
+constexpr int kSC = 8;      // head-dim chunk
+constexpr int kSP = kST + 2; // LDS row stride in doubles (16-byte aligned rows)
 __global__ __launch_bounds__(256) void mask_scores_kernel(const ScoreArgs a) {
-    __shared__ double As[16][65];
-    __shared__ double Bs[16][65];
+    __shared__ __attribute__((aligned(16))) double As[2][kSC][kSP];
+    __shared__ __attribute__((aligned(16))) double Bs[2][kSC][kSP];
     const int tid = threadIdx.x, tr = tid / 16, tc = tid % 16;
-    const int j0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+    const int j0 = blockIdx.x * kST, r0 = blockIdx.y * kST;
     const int bg = blockIdx.z, b = bg / a.Hkv, g = bg % a.Hkv;
     const int R = a.G * a.nb;
-    // rows r = hl * nb + i of the kv head's query heads; skip tiles entirely above the diagonal
-    const int rl = min(r0 + 63, R - 1);
+    const int rl = min(r0 + kST - 1, R - 1);
     const int imax = (r0 / a.nb == rl / a.nb) ? rl % a.nb : a.nb - 1;
     if (j0 > imax) return;
     const double* kb = a.kbar + ((size_t)b * a.Hkv + g) * a.nb * a.D;
-    double acc[4][4];
+    // loader: thread -> (row or key block lr = tid / 2, head-dim half lh = tid % 2: 4 doubles)
+    const int lr = tid / 2, lh = tid % 2;
+    const int ra = r0 + lr, ja = j0 + lr;
+    const double* qsrc = nullptr;
+    if (ra < R) {
+        const int hl = ra / a.nb, i = ra % a.nb;
+        qsrc = a.qbar + (((size_t)b * a.Hq + g * a.G + hl) * a.nb + i) * a.D + 4 * lh;
+    }
+    const double* ksrc = ja < a.nb ? kb + (size_t)ja * a.D + 4 * lh : nullptr;
+    auto fetch = [&](int d0, double (&qa)[4], double (&ka)[4]) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
-    for (int d0 = 0; d0 < a.D; d0 += 16) {
-        __syncthreads();
-        for (int e = tid; e < 16 * 64; e += 256) {
-            const int rr = e / 16, dd = e % 16;
-            const int r = r0 + rr, j = j0 + rr;
-            double av = 0.0, bv = 0.0;
-            if (r < R) {
-                const int hl = r / a.nb, i = r % a.nb;
-                av = a.qbar[(((size_t)b * a.Hq + g * a.G + hl) * a.nb + i) * a.D + d0 + dd];
-            }
-            if (j < a.nb) bv = kb[(size_t)j * a.D + d0 + dd];
-            As[dd][rr] = av;
-            Bs[dd][rr] = bv;
+        for (int k = 0; k < 4; ++k) {
+            qa[k] = qsrc ? qsrc[d0 + k] : 0.0;
+            ka[k] = ksrc ? ksrc[d0 + k] : 0.0;
         }
-        __syncthreads();
+    };
+    auto stash = [&](int buf, const double (&qa)[4], const double (&ka)[4]) {
 #pragma unroll
-        for (int dd = 0; dd < 16; ++dd) {
-            double x[4], y[4];
+        for (int k = 0; k < 4; ++k) {
+            As[buf][4 * lh + k][lr] = qa[k];
+            Bs[buf][4 * lh + k][lr] = ka[k];
+        }
+    };
+    double acc[8][8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                x[u] = As[dd][tr * 4 + u];
-                y[u] = Bs[dd][tc * 4 + u];
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[u][v] = 0.0;
+    double qa[4], ka[4];
+    fetch(0, qa, ka);
+    stash(0, qa, ka);
+    __syncthreads();
+    const int nch = a.D / kSC;
+    for (int ch = 0; ch < nch; ++ch) {
+        const int buf = ch & 1;
+        if (ch + 1 < nch) fetch((ch + 1) * kSC, qa, ka);
+#pragma unroll
+        for (int dd = 0; dd < kSC; ++dd) {
+            double x[8], y[8];
+#pragma unroll
+            for (int u = 0; u < 8; u += 2) {
+                const double2 t = *reinterpret_cast<const double2*>(&As[buf][dd][8 * tr + u]);
+                x[u] = t.x;
+                x[u + 1] = t.y;
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int k = 0; k < 4; ++k) {
+                const double2 t = *reinterpret_cast<const double2*>(&Bs[buf][dd][32 * k + 2 * tc]);
+                y[2 * k] = t.x;
+                y[2 * k + 1] = t.y;
+            }
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[u][v] = fma(x[u], y[v], acc[u][v]);
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int v = 0; v < 8; ++v) acc[u][v] = fma(x[u], y[v], acc[u][v]);
         }
+        if (ch + 1 < nch) stash(buf ^ 1, qa, ka);
+        __syncthreads();
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int r = r0 + tr * 4 + u;
+    for (int u = 0; u < 8; ++u) {
+        const int r = r0 + 8 * tr + u;
         if (r >= R) continue;
         const int hl = r / a.nb, i = r % a.nb;
         double* srow = a.scores + (((size_t)b * a.Hq + g * a.G + hl) * a.nb + i) * a.nb;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int j = j0 + tc * 4 + v;
+        for (int v = 0; v < 8; ++v) {
+            const int j = j0 + 32 * (v / 2) + 2 * tc + (v % 2);
             if (j <= i && j < a.nb) srow[j] = __dmul_rn(a.scale, acc[u][v]);
         }
     }
@@ -409,7 +440,8 @@ hipError_t launch_block_mask(const MaskProblem& p, const MaskWorkspace& ws, hipS
     sc.nb = p.nb;
     sc.D = p.D;
     sc.scale = p.scale;
-    const dim3 sgrid((unsigned)((p.nb + 63) / 64), (unsigned)((sc.G * p.nb + 63) / 64), (unsigned)(p.B * p.Hkv));
+    const dim3 sgrid((unsigned)((p.nb + kST - 1) / kST), (unsigned)((sc.G * p.nb + kST - 1) / kST),
+                     (unsigned)(p.B * p.Hkv));
     hipLaunchKernelGGL(mask_scores_kernel, sgrid, dim3(256), 0, s, sc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
