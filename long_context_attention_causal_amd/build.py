@@ -26,10 +26,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-t
 # Per-source extras. The prefill kernels' row maxima see no NaN unless the inputs hold one (the output is then NaN
 # regardless), so they are built without NaN semantics: a max then needs no quieting of its inputs, which otherwise
 # doubles the VALU work of every tile's row-max reduction. Infinities keep their meaning (masked scores are -inf).
-# They are also scheduled for instruction-level parallelism rather than the default occupancy-first strategy: each
-# wave's QK, softmax and PV of a tile are one long dependent stretch, and the ILP schedule overlaps more of it (dense
-# N=4096 3% and the 32K block-sparse workload 3% faster on one machine, same output bits).
-EXTRA = {"prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+EXTRA = {"prefill.hip": ["-fno-honor-nans"]}
 
 
 def sources():
