@@ -110,8 +110,8 @@ def _check(status: int) -> None:
         raise LcattnError(status, load().attn_last_error().decode(errors="replace"))
 
 
-def _stream(stream) -> ctypes.c_void_p:
-    s = stream if stream is not None else torch.cuda.current_stream()
+def _stream(stream, device: torch.device) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -132,6 +132,21 @@ def _need(t: torch.Tensor, name: str, dtype=None, ndim=None) -> None:
         raise LcattnError(2, f"{name} must have {ndim} dims")
 
 
+def _like(t: torch.Tensor, name: str, shape, dtype, device: torch.device) -> None:
+    """A caller-supplied output or workspace must match exactly: the library gets plain pointers and trusts sizes."""
+    _need(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise LcattnError(2, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise LcattnError(2, f"{name} is on {t.device}, the inputs on {device}")
+
+
+def _same_device(device: torch.device, *named) -> None:
+    for t, n in named:
+        if t.device != device:
+            raise LcattnError(2, f"{n} is on {t.device}, q on {device}")
+
+
 def _prefill_shape(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float]) -> AttnShape:
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise LcattnError(3, "q must be bf16 or fp32")
@@ -140,6 +155,7 @@ def _prefill_shape(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Opt
     B, Hq, N, D = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != D:
         raise LcattnError(2, f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    _same_device(q.device, (k, "k"), (v, "v"))
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     return AttnShape(B, Hq, k.shape[1], N, D, sc, ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_FP32)
 
@@ -151,9 +167,10 @@ def prefill_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Opti
     lib = load()
     shp = _prefill_shape(q, k, v, scale)
     o = torch.empty_like(q) if out is None else out
-    _need(o, "out", q.dtype)
+    _like(o, "out", q.shape, q.dtype, q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
-    _check(lib.attn_prefill_dense(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(stream)))
+    _check(lib.attn_prefill_dense(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                  _stream(stream, q.device)))
     return o, lse
 
 
@@ -183,9 +200,9 @@ def block_mask_build(q: torch.Tensor, k: torch.Tensor, block_size: int, keep_per
     shp = _prefill_shape(q, k, k, scale)
     prm = AttnMaskParams(block_size, keep_permille, float(rescue_alpha), q_lo_pct, q_hi_pct)
     need = int(lib.attn_block_mask_workspace_bytes(ctypes.byref(shp), ctypes.byref(prm)))
-    if need == 0:
+    if need == 0:   # the library rejects these parameters; this call reports why
         _check(lib.attn_block_mask_build(ctypes.byref(shp), ctypes.byref(prm), _ptr(q), _ptr(k), None, None, None,
-                                         None, None, 0, _stream(stream)))
+                                         None, None, 0, _stream(stream, q.device)))
     B, Hq, N, _ = q.shape
     Hkv = k.shape[1]
     nb = N // block_size
@@ -198,9 +215,16 @@ def block_mask_build(q: torch.Tensor, k: torch.Tensor, block_size: int, keep_per
                             radius_stats=(torch.empty((B, Hkv, nb + 3), dtype=torch.float64, device=dev)
                                           if want_radius_stats else None),
                             workspace=ws)
+    _like(outputs.mask, "mask", (B, Hq, nb, nb), torch.uint8, dev)
+    _like(outputs.kv_count, "kv_count", (B, Hq, nb), torch.int32, dev)
+    _like(outputs.kv_index, "kv_index", (B, Hq, nb, nb), torch.int32, dev)
+    if outputs.radius_stats is not None:
+        _like(outputs.radius_stats, "radius_stats", (B, Hkv, nb + 3), torch.float64, dev)
+    _need(outputs.workspace, "workspace", torch.uint8)
+    _same_device(dev, (outputs.workspace, "workspace"))
     _check(lib.attn_block_mask_build(ctypes.byref(shp), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(outputs.mask),
                                      _ptr(outputs.kv_count), _ptr(outputs.kv_index), _ptr(outputs.radius_stats),
-                                     _ptr(outputs.workspace), outputs.workspace.numel(), _stream(stream)))
+                                     _ptr(outputs.workspace), outputs.workspace.numel(), _stream(stream, dev)))
     return outputs
 
 
@@ -217,11 +241,13 @@ def prefill_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_c
     _need(kv_index, "kv_index", torch.int32)
     if tuple(kv_count.shape) != (B, Hq, nb) or tuple(kv_index.shape) != (B, Hq, nb, nb):
         raise LcattnError(2, "kv_count/kv_index shapes do not match q and block_size")
+    _same_device(q.device, (kv_count, "kv_count"), (kv_index, "kv_index"))
     o = torch.empty_like(q) if out is None else out
-    _need(o, "out", q.dtype)
+    _like(o, "out", q.shape, q.dtype, q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
     _check(lib.attn_prefill_block_sparse(ctypes.byref(shp), int(block_size), _ptr(q), _ptr(k), _ptr(v),
-                                         _ptr(kv_count), _ptr(kv_index), _ptr(o), _ptr(lse), _stream(stream)))
+                                         _ptr(kv_count), _ptr(kv_index), _ptr(o), _ptr(lse),
+                                         _stream(stream, q.device)))
     return o, lse
 
 
@@ -254,13 +280,19 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     _need(seq_lens, "seq_lens", torch.int32, 1)
     if k_cache.shape != v_cache.shape:
         raise LcattnError(2, "k_cache and v_cache shapes differ")
+    if block_table.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
+        raise LcattnError(2, "block_table and seq_lens need one row per sequence of q")
+    _same_device(q.device, (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens"))
     shp = _decode_shape(q, k_cache, block_table, chunk_tokens, scale)
     need = int(lib.attn_decode_workspace_bytes(ctypes.byref(shp), int(max_seq_len)))
     ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _need(ws, "workspace", torch.uint8)
+    _same_device(q.device, (ws, "workspace"))
     o = torch.empty_like(q) if out is None else out
-    _need(o, "out", torch.bfloat16)
+    _like(o, "out", q.shape, torch.bfloat16, q.device)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if return_lse else None
     _check(lib.attn_decode_paged(ctypes.byref(shp), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                  _ptr(seq_lens), int(max_seq_len), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
-                                 _stream(stream)))
+                                 _stream(stream, q.device)))
     return o, lse

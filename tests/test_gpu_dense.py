@@ -121,3 +121,32 @@ def test_dense_long_sampled(lib, name, per_head):
     eo, el = max_err(og, Oref), max_err(lg, Lref)
     say(f"[dense] {name}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
     assert eo <= BF16_TOL and el <= LSE_TOL
+
+
+def test_binding_rejects_mismatched_buffers(lib):
+    """The library gets plain pointers and trusts sizes: the binding refuses wrong-sized outputs and workspaces
+    before anything is launched."""
+    dev = torch.device("cuda", 0)
+    q = torch.zeros(1, 4, 64, 64, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(lib.LcattnError):
+        lib.prefill_dense(q, k, k, out=torch.empty(1, 4, 63, 64, dtype=torch.bfloat16, device=dev))
+    with pytest.raises(lib.LcattnError):
+        lib.prefill_dense(q, k, k, out=torch.empty(1, 4, 64, 64, dtype=torch.float32, device=dev))
+    cnt = torch.ones(1, 4, 1, dtype=torch.int32, device=dev)
+    idx = torch.zeros(1, 4, 1, 1, dtype=torch.int32, device=dev)
+    with pytest.raises(lib.LcattnError):
+        lib.prefill_block_sparse(q, k, k, cnt, idx, 64, out=torch.empty(2, 4, 64, 64, dtype=torch.bfloat16,
+                                                                          device=dev))
+    m = lib.block_mask_build(q, k, 64, 100, 1.0)
+    m.kv_index = torch.empty(1, 4, 1, 2, dtype=torch.int32, device=dev)
+    with pytest.raises(lib.LcattnError):
+        lib.block_mask_build(q, k, 64, 100, 1.0, outputs=m)
+    q1 = torch.zeros(2, 4, 64, dtype=torch.bfloat16, device=dev)
+    kc = torch.zeros(8, 2, 16, 64, dtype=torch.bfloat16, device=dev)
+    bt = torch.zeros(2, 4, dtype=torch.int32, device=dev)
+    with pytest.raises(lib.LcattnError):   # one sequence length for two sequences
+        lib.decode_paged(q1, kc, kc, bt, torch.ones(1, dtype=torch.int32, device=dev), 64)
+    with pytest.raises(lib.LcattnError):   # workspace of the wrong element type
+        lib.decode_paged(q1, kc, kc, bt, torch.ones(2, dtype=torch.int32, device=dev), 64,
+                         workspace=torch.empty(1 << 20, dtype=torch.float32, device=dev))
