@@ -143,6 +143,30 @@ def main():
     per = np.array([[r[i].elapsed_time(r[i + 1]) for i in range(4)] for r in recs])   # ms per part
     t_dense, t_mask3, t_sparse3, t_dec = (float(x) for x in per.mean(axis=0))
 
+    def spread(x):   # median and the 10th / 90th percentiles of per-call times, ms
+        x = np.asarray(x, dtype=np.float64)
+        return {"ms_median": float(np.median(x)), "ms_p10": float(np.percentile(x, 10)),
+                "ms_p90": float(np.percentile(x, 90))}
+
+    # decode timed cold as well: 1 GiB read between calls evicts L2 and the 256 MB last-level cache (a read rather than
+    # a write, whose dirty lines would be written back during the decode and charge it for the eviction)
+    log("paged decode, cold (1 GiB read between calls)")
+    junk = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for i in range(args.steps + 2):
+        junk.sum()
+        a_, b_ = ev(), ev()
+        a_.record()
+        lca.decode_paged(q5, kc5, vc5, bt5, sl5, maxlen5, w5["chunk"], scale=c5.scale, out=o5, return_lse=False,
+                         workspace=ws5)
+        b_.record()
+        if i >= 2:
+            cold.append((a_, b_))
+    torch.cuda.synchronize()
+    cold_ms = [a_.elapsed_time(b_) for a_, b_ in cold]
+    del junk
+    torch.cuda.empty_cache()
+
     B, Hq, N, D = c2.q.shape
     fl2 = dense_flops(B, Hq, N, D)
     tflops2 = fl2 / (t_dense * 1e-3) / 1e12
@@ -167,16 +191,19 @@ def main():
     mask_read3 = float((w3["Hq"] + w3["Hkv"]) * w3["N"] * D3 * 2)
 
     paths = {
-        "dense_prefill_n4096": {"ms": t_dense, "tflops": tflops2, "pct_bf16_peak": 100 * tflops2 / PEAK_BF16_TFLOPS,
-                                "tokens_per_s": N / (t_dense * 1e-3)},
-        "mask_build_n32768_b64": {"ms": t_mask3, "stats_read_bytes": mask_read3,
+        "dense_prefill_n4096": {"ms": t_dense, **spread(per[:, 0]), "tflops": tflops2,
+                                "pct_bf16_peak": 100 * tflops2 / PEAK_BF16_TFLOPS, "tokens_per_s": N / (t_dense * 1e-3)},
+        "mask_build_n32768_b64": {"ms": t_mask3, **spread(per[:, 1]), "stats_read_bytes": mask_read3,
                                   "stats_read_gbs_over_whole_build": mask_read3 / (t_mask3 * 1e-3) / 1e9,
                                   "density": density3},
-        "sparse_prefill_n32768_b64": {"ms": t_sparse3, "executed_tflop": exec3 / 1e12,
+        "sparse_prefill_n32768_b64": {"ms": t_sparse3, **spread(per[:, 2]), "executed_tflop": exec3 / 1e12,
                                       "executed_tflops": exec3 / (t_sparse3 * 1e-3) / 1e12,
                                       "pct_bf16_peak_executed": 100 * exec3 / (t_sparse3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                       "dense_equiv_tflops_incl_mask": dense_eq3 / ((t_sparse3 + t_mask3) * 1e-3) / 1e12},
-        "decode_paged_c5": {"ms": t_dec, "algorithmic_bytes": dec_bytes, "gbs": dec_gbs,
+        "decode_paged_c5": {"ms": t_dec, **spread(per[:, 3]), "algorithmic_bytes": dec_bytes, "gbs": dec_gbs,
+                            "cold_ms": float(np.mean(cold_ms)), "cold_ms_median": float(np.median(cold_ms)),
+                            "cold_gbs": dec_bytes / (float(np.mean(cold_ms)) * 1e-3) / 1e9,
+                            "cold_pct_hbm_peak": 100 * dec_bytes / (float(np.mean(cold_ms)) * 1e-3) / 1e9 / PEAK_HBM_GBS,
                             "measured_hbm_bytes": (lambda a, b: None if a is None or b is None else a + b)(
                                 measured_traffic("decode_split_c5", "decode.hip"),
                                 measured_traffic("decode_combine_c5", "decode.hip")),
@@ -195,14 +222,15 @@ def main():
             b.record()
             es.append((a, b))
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in es]))
+        x = [a.elapsed_time(b) for a, b in es]
+        return float(np.mean(x)), spread(x)
 
     if not args.no_long:
         log("dense prefill at 32K")
-        t32 = time_calls(lambda: lca.prefill_dense(q3, k3, v3, scale=c3.scale, out=o3, return_lse=False),
-                         max(args.long_reps, 5))
+        t32, s32 = time_calls(lambda: lca.prefill_dense(q3, k3, v3, scale=c3.scale, out=o3, return_lse=False),
+                              max(args.long_reps, 5))
         tf32 = dense_eq3 / (t32 * 1e-3) / 1e12
-        paths["dense_prefill_n32768"] = {"ms": t32, "tflops": tf32, "pct_bf16_peak": 100 * tf32 / PEAK_BF16_TFLOPS}
+        paths["dense_prefill_n32768"] = {"ms": t32, **s32, "tflops": tf32, "pct_bf16_peak": 100 * tf32 / PEAK_BF16_TFLOPS}
         paths["sparse_prefill_n32768_b64"]["speedup_vs_dense_kernel_only"] = t32 / t_sparse3
         paths["sparse_prefill_n32768_b64"]["speedup_vs_dense_incl_mask"] = t32 / (t_sparse3 + t_mask3)
         del q3, k3, v3, o3, m3
@@ -214,26 +242,27 @@ def main():
         o4 = torch.empty_like(q4)
         del c4
         log("dense prefill at 128K")
-        t128 = time_calls(lambda: lca.prefill_dense(q4, k4, v4, scale=1 / math.sqrt(128), out=o4, return_lse=False),
-                          args.long_reps)
+        t128, s128 = time_calls(lambda: lca.prefill_dense(q4, k4, v4, scale=1 / math.sqrt(128), out=o4,
+                                                          return_lse=False), args.long_reps)
         fl128 = dense_flops(1, w4["Hq"], w4["N"], w4["D"])
         tf128 = fl128 / (t128 * 1e-3) / 1e12
-        paths["dense_prefill_n131072"] = {"ms": t128, "tflops": tf128, "pct_bf16_peak": 100 * tf128 / PEAK_BF16_TFLOPS}
+        paths["dense_prefill_n131072"] = {"ms": t128, **s128, "tflops": tf128,
+                                          "pct_bf16_peak": 100 * tf128 / PEAK_BF16_TFLOPS}
         log("mask build + sparse prefill at 128K")
         m4 = lca.block_mask_build(q4, k4, w4["block"], w4["keep_permille"], w4["alpha"], w4["q_lo_pct"],
                                   w4["q_hi_pct"], scale=1 / math.sqrt(128), want_radius_stats=False)
-        tm4 = time_calls(lambda: lca.block_mask_build(q4, k4, w4["block"], w4["keep_permille"], w4["alpha"],
-                                                      w4["q_lo_pct"], w4["q_hi_pct"], scale=1 / math.sqrt(128),
-                                                      outputs=m4), args.long_reps)
-        ts4 = time_calls(lambda: lca.prefill_block_sparse(q4, k4, v4, m4.kv_count, m4.kv_index, w4["block"],
-                                                          scale=1 / math.sqrt(128), out=o4, return_lse=False),
-                         args.long_reps)
+        tm4, _ = time_calls(lambda: lca.block_mask_build(q4, k4, w4["block"], w4["keep_permille"], w4["alpha"],
+                                                         w4["q_lo_pct"], w4["q_hi_pct"], scale=1 / math.sqrt(128),
+                                                         outputs=m4), args.long_reps)
+        ts4, sts4 = time_calls(lambda: lca.prefill_block_sparse(q4, k4, v4, m4.kv_count, m4.kv_index, w4["block"],
+                                                                scale=1 / math.sqrt(128), out=o4, return_lse=False),
+                               args.long_reps)
         cnt4 = m4.kv_count.cpu().numpy().astype(np.int64)
         b4 = w4["block"]
         exec4 = float(((cnt4 - 1) * 4.0 * b4 * b4 * w4["D"] + 2.0 * b4 * (b4 + 1) * w4["D"]).sum())
         nb4 = w4["N"] // b4
         paths["sparse_prefill_n131072_b128"] = {
-            "mask_ms": tm4, "sparse_ms": ts4, "density": float(cnt4.sum() / (w4["Hq"] * nb4 * (nb4 + 1) / 2)),
+            "mask_ms": tm4, "sparse_ms": ts4, "sparse_ms_median": sts4["ms_median"], "density": float(cnt4.sum() / (w4["Hq"] * nb4 * (nb4 + 1) / 2)),
             "executed_tflops": exec4 / (ts4 * 1e-3) / 1e12,
             "pct_bf16_peak_executed": 100 * exec4 / (ts4 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "dense_equiv_tflops_incl_mask": fl128 / ((ts4 + tm4) * 1e-3) / 1e12,
