@@ -12,13 +12,28 @@ the method in outline; the steps below are its order, with the open points fixed
  3. Per (batch, kv-head), over all key blocks: the median and the 90th percentile of the radii, as type-7
     linear-interpolated quantiles (numpy's default method) at integer percentages, evaluated with exact integer
     index arithmetic; then the rescue threshold tau = med + alpha * (p90 - med).
- 4. Rescue branch: key block j is flagged when r_j > tau (strict), for every query head of the kv-head's group.
+ 4. Rescue branch: key block j is flagged when r_j > tau (strict), for every query head of the kv-head's group
+    (rescue_mode 0; the query-aware form, rescue_mode 1, follows below).
  5. Centroid branch: for query block i of head h, the candidates are the causally visible key blocks j <= i;
     their score is scale * <mean q-block, key centroid>; the k_i = ceil((i+1) * keep_permille / 1000) best are
     kept (integer ceiling), ties broken towards the smaller j.
  6. The two branches are thresholded independently and OR-ed, and the diagonal block is always kept:
-    M[h,i,j] = 1 iff j <= i and (centroid-kept or rescue-flagged or j == i).
+    M[h,i,j] = 1 iff j <= i and (centroid-kept or rescued or j == i).
  7. The kept list of each (h, i) row, ascending in j, is the CSR form the sparse kernel walks.
+
+Step 4 has two forms. rescue_mode 0 is the query-blind test above: every flagged block is rescued for every row
+that can see it. rescue_mode 1 reads the section's last step -- the radius distribution yields a coefficient,
+and the rescue candidates are then scored against the base path with it -- as follows:
+ 4a. coefficient lambda = (p90 - med) / p90 per (batch, kv-head), the spread of the radii between the two
+     reference points relative to the upper one (0 when p90 is 0); it lies in [0, 1];
+ 4b. the candidates of row (h, i) are the blocks j <= i flagged by the radius test of step 4;
+ 4c. a candidate's rescue score is its centroid score plus lambda times the Cauchy-Schwarz allowance of the
+     part of its radius above the median, U_ij = S_ij + lambda * scale * |qbar_i| * (r_j - med): with lambda = 1
+     and med = 0 this is the upper bound of <qbar_i, key> * scale over the block's keys;
+ 4d. the candidate is rescued for that row when U_ij > the base branch's cutoff in the same row (the k_i-th
+     largest centroid score; no cutoff, so no rescue, when k_i = 0).
+ Mode 1 therefore rescues a subset of what mode 0 rescues, row by row, and a query block whose mean is far from
+ a wide block's outlier direction no longer pays for it.
 """
 from __future__ import annotations
 
@@ -78,6 +93,12 @@ def rescue_threshold(radii: np.ndarray, alpha: float, lo_pct: int = 50, hi_pct: 
     return med, hi, float(tau)
 
 
+def rescue_coefficient(med: float, hi: float) -> float:
+    """Step 4a: lambda = (p90 - med) / p90, and 0 when p90 is 0 (then at least the upper tenth of the radii are
+    zero, every block above the median is a single point, and no allowance is owed)."""
+    return 0.0 if hi == 0.0 else (hi - med) / hi
+
+
 def centroid_budget(i: int, keep_permille: int) -> int:
     """k_i = ceil((i+1) * keep_permille / 1000) in integer arithmetic."""
     return ((i + 1) * int(keep_permille) + 999) // 1000
@@ -96,11 +117,18 @@ class MaskResult:
     centroid: np.ndarray     # bool [B,Hq,nQB,nKB]: the centroid branch alone (before the OR)
     cut_gap: np.ndarray      # float64 [B,Hq,nQB]: score of the last kept minus the best dropped (inf if none)
     score_absmax: np.ndarray  # float64 [B,Hq,nQB]: max |score| over the row's candidates
+    rescued: np.ndarray      # bool [B,Hq,nQB,nKB]: the rescue branch alone, per row (mode 0: rescue broadcast)
+    lam: np.ndarray          # float64 [B,Hkv]: step 4a coefficient (computed in both modes)
+    qnorm: np.ndarray        # float64 [B,Hq,nQB]: |qbar_i|
+    rescue_gap: np.ndarray   # float64 [B,Hq,nQB]: mode 1, min over deciding candidates of |U - cut| relative to
+                             # 1 + |S| + |allowance| + |cut| (inf if none, and always inf in mode 0)
 
 
 def build_mask(q: np.ndarray, k: np.ndarray, scale: float, block: int, keep_permille: int, alpha: float,
-               lo_pct: int = 50, hi_pct: int = 90) -> MaskResult:
-    """Steps 1-7 on float64 inputs q [B,Hq,N,D], k [B,Hkv,N,D]."""
+               lo_pct: int = 50, hi_pct: int = 90, rescue_mode: int = 0) -> MaskResult:
+    """Steps 1-7 on float64 inputs q [B,Hq,N,D], k [B,Hkv,N,D]; rescue_mode 0 or 1 selects step 4's form."""
+    if rescue_mode not in (0, 1):
+        raise ValueError("rescue_mode must be 0 or 1")
     B, Hq, N, D = q.shape
     Hkv = k.shape[1]
     if Hq % Hkv:
@@ -115,9 +143,13 @@ def build_mask(q: np.ndarray, k: np.ndarray, scale: float, block: int, keep_perm
         for g in range(Hkv):
             med[b, g], p90[b, g], tau[b, g] = rescue_threshold(rad[b, g], alpha, lo_pct, hi_pct)
     rescue = rad > tau[:, :, None]
+    lam = np.array([[rescue_coefficient(med[b, g], p90[b, g]) for g in range(Hkv)] for b in range(B)])
+    qnorm = np.sqrt((qbar * qbar).sum(axis=3))
     mask = np.zeros((B, Hq, nb, nb), dtype=np.uint8)
     cen = np.zeros((B, Hq, nb, nb), dtype=bool)
+    resc = np.zeros((B, Hq, nb, nb), dtype=bool)
     gap = np.full((B, Hq, nb), np.inf)
+    rgap = np.full((B, Hq, nb), np.inf)
     amax = np.zeros((B, Hq, nb))
     for b in range(B):
         for h in range(Hq):
@@ -133,7 +165,22 @@ def build_mask(q: np.ndarray, k: np.ndarray, scale: float, block: int, keep_perm
                 cen[b, h, i, kept] = True
                 if 0 < kk < i + 1:
                     gap[b, h, i] = s[order[kk - 1]] - s[order[kk]]
-                row = cen[b, h, i, :i + 1] | rescue[b, g, :i + 1]
+                cand = rescue[b, g, :i + 1]
+                if rescue_mode == 0:
+                    r_row = cand.copy()
+                else:
+                    cut = s[order[kk - 1]] if kk > 0 else np.inf
+                    coef = lam[b, g] * scale * qnorm[b, h, i]
+                    allow = coef * (rad[b, g, :i + 1] - med[b, g])
+                    u = s + allow
+                    r_row = cand & (u > cut)
+                    # decisions that can change the mask: candidates outside the centroid pick, off the diagonal
+                    deciding = cand & ~cen[b, h, i, :i + 1] & (j != i)
+                    if np.isfinite(cut) and deciding.any():
+                        rel = np.abs(u - cut) / (1.0 + np.abs(s) + np.abs(allow) + abs(cut))
+                        rgap[b, h, i] = rel[deciding].min()
+                resc[b, h, i, :i + 1] = r_row
+                row = cen[b, h, i, :i + 1] | r_row
                 row[i] = True
                 mask[b, h, i, :i + 1] = row
     kv_count = mask.sum(axis=3, dtype=np.int64).astype(np.int32)
@@ -144,4 +191,5 @@ def build_mask(q: np.ndarray, k: np.ndarray, scale: float, block: int, keep_perm
                 idx = np.nonzero(mask[b, h, i])[0]
                 kv_index[b, h, i, :len(idx)] = idx
     return MaskResult(mask=mask, kv_count=kv_count, kv_index=kv_index, radius=rad, med=med, p90=p90, tau=tau,
-                      rescue=rescue, centroid=cen, cut_gap=gap, score_absmax=amax)
+                      rescue=rescue, centroid=cen, cut_gap=gap, score_absmax=amax, rescued=resc, lam=lam,
+                      qnorm=qnorm, rescue_gap=rgap)

@@ -185,3 +185,133 @@ def test_rescue_comparison_is_strict():
     assert res.tau[0, 0] == res.radius[0, 0, 0]
     assert res.rescue[0, 0].tolist() == [False, True, False, True, False]
     assert res.mask[0, 0, 4].nonzero()[0].tolist() == [1, 3, 4]
+
+
+# -------------------------------------------------------------------------------- query-aware rescue (mode 1)
+def _two_axis_keys(radii, xs, b=2):
+    """Key block j holds (x_j, +r_j) and (x_j, -r_j) (b = 2): centroid (x_j, 0), radius exactly r_j."""
+    nb = len(radii)
+    k = np.zeros((1, 1, b * nb, 2))
+    for j, (r, x) in enumerate(zip(radii, xs)):
+        k[0, 0, b * j] = (x, r)
+        k[0, 0, b * j + 1] = (x, -r)
+    return k
+
+
+def test_rescue_coefficient_closed_forms():
+    assert M.rescue_coefficient(4.0, 12.0) == 8.0 / 12.0
+    assert M.rescue_coefficient(3.0, 3.0) == 0.0           # no spread between the reference points
+    assert M.rescue_coefficient(0.0, 0.0) == 0.0           # degenerate: p90 = 0
+    assert M.rescue_coefficient(0.0, 5.0) == 1.0
+
+
+def test_query_aware_rescue_hand_case():
+    """Six key blocks of two keys in 2-D with radii 15, 5, 9, 1, 2, 3 (sorted 1 2 3 5 9 15: median 4, 90th
+    percentile 12, lambda = 2/3). Head 0's last query block has mean (0.9, 1.2), norm 1.5, so its allowance per
+    unit of excess radius is lambda * 1.5 = 1; its centroid scores 0.9 * x_j are, per block,
+    -13, -0.85, -5.2, 0, -0.3, +1 and keep_permille 300 keeps two (blocks 5 and 3, cutoff 0).
+    alpha = 0 makes blocks 0, 1, 2 (radius > 4) candidates with excess 11, 1, 5:
+      U = -13 + 11 = -2 (no), -0.85 + 1 = 0.15 (rescued), -5.2 + 5 = -0.2 (no).
+    Every other query block is zero (all scores tie at 0, cutoff 0, allowance 0: nothing is rescued, the centroid
+    branch keeps the first k_i blocks). A dropped or squared query norm, the full radius instead of the excess, a
+    coefficient of 1 or (p90 - med) / med, the wrong rank for the cutoff, a flipped sign or a missing candidate
+    filter each change head 0's last row."""
+    radii = [15.0, 5.0, 9.0, 1.0, 2.0, 3.0]
+    target = [-13.0, -0.85, -5.2, 0.0, -0.3, 1.0]
+    k = _two_axis_keys(radii, [t / 0.9 for t in target])
+    q = np.zeros((1, 2, 12, 2))
+    q[0, 0, 10:12] = (0.9, 1.2)
+    res = M.build_mask(q, k, 1.0, 2, keep_permille=300, alpha=0.0, rescue_mode=1)
+    assert (res.med[0, 0], res.p90[0, 0]) == (4.0, 12.0)
+    assert abs(res.qnorm[0, 0, 5] - 1.5) < 1e-15
+    rows = lambda h: [res.mask[0, h, i].nonzero()[0].tolist() for i in range(6)]
+    first = [[0], [0, 1], [0, 2], [0, 1, 3], [0, 1, 4]]
+    assert rows(0) == first + [[1, 3, 5]]
+    assert rows(1) == first + [[0, 1, 5]]
+    # the query-blind rule rescues all three candidates in every row that sees them
+    blind = M.build_mask(q, k, 1.0, 2, keep_permille=300, alpha=0.0, rescue_mode=0)
+    assert blind.mask[0, 0, 5].nonzero()[0].tolist() == [0, 1, 2, 3, 5]
+    # alpha = 0.5 raises tau to 8: block 1 (radius 5) is no longer a candidate
+    half = M.build_mask(q, k, 1.0, 2, keep_permille=300, alpha=0.5, rescue_mode=1)
+    assert half.mask[0, 0, 5].nonzero()[0].tolist() == [3, 5]
+
+
+def test_query_aware_rescue_is_strict():
+    """Exactly representable case: radii 5 3 3 1 1 1 (median 2, 90th percentile 4, lambda 1/2), query mean (2, 0)
+    (allowance 1 per unit of excess), scores 2 * x_j = -1, 1, 1.5, 2, 0, 4, cutoff 2 (blocks 5 and 3). Blocks 0
+    and 1 land exactly on the cutoff (U = -1 + 3 = 2, 1 + 1 = 2) and are not rescued; block 2 (U = 2.5) is."""
+    k = _two_axis_keys([5.0, 3.0, 3.0, 1.0, 1.0, 1.0], [-0.5, 0.5, 0.75, 1.0, 0.0, 2.0])
+    q = np.zeros((1, 1, 12, 2))
+    q[0, 0, 10:12] = (2.0, 0.0)
+    res = M.build_mask(q, k, 1.0, 2, keep_permille=300, alpha=0.0, rescue_mode=1)
+    assert res.lam[0, 0] == 0.5
+    assert res.mask[0, 0, 5].nonzero()[0].tolist() == [2, 3, 5]
+    assert res.rescue_gap[0, 0, 5] == 0.0
+
+
+def brute_mask_query_aware(qbar, kbar, rad, scale, keep, alpha, G):
+    """Pure-Python statement of the mode-1 rule for tiny sizes."""
+    B, Hq, nb, D = qbar.shape
+    out = np.zeros((B, Hq, nb, nb), dtype=np.uint8)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            xs = sorted(float(r) for r in rad[b, g])
+            med = float(np.quantile(xs, 0.5))
+            hi = float(np.quantile(xs, 0.9))
+            tau = math.inf if math.isinf(alpha) else med + alpha * (hi - med)
+            lam = 0.0 if hi == 0 else (hi - med) / hi
+            for i in range(nb):
+                qn = math.sqrt(sum(v * v for v in qbar[b, h, i]))
+                score = {j: scale * sum(qbar[b, h, i, d] * kbar[b, g, j, d] for d in range(D)) for j in range(i + 1)}
+                budget = math.ceil(Fraction((i + 1) * keep, 1000))
+                ranked = sorted(range(i + 1), key=lambda j: (-score[j], j))
+                cut = score[ranked[budget - 1]] if budget > 0 else math.inf
+                for j in range(i + 1):
+                    rescued = rad[b, g, j] > tau and score[j] + lam * scale * qn * (rad[b, g, j] - med) > cut
+                    if j in ranked[:budget] or rescued or j == i:
+                        out[b, h, i, j] = 1
+    return out
+
+
+@pytest.mark.parametrize("keep,alpha", [(100, 1.0), (300, 0.5), (200, 0.0), (0, 0.0), (250, math.inf)])
+def test_query_aware_mask_equals_enumeration(keep, alpha):
+    b, nb = 4, 10
+    q, k = rnd(60, 1, 4, b * nb, 3), rnd(61, 1, 2, b * nb, 3)
+    res = M.build_mask(q, k, 0.7, b, keep, alpha, rescue_mode=1)
+    qbar, kbar, rad = M.block_stats(q, k, b)
+    assert np.isfinite(res.rescue_gap[np.isfinite(res.rescue_gap)]).all()
+    np.testing.assert_array_equal(res.mask, brute_mask_query_aware(qbar, kbar, rad, 0.7, keep, alpha, 2))
+
+
+def test_query_aware_rescue_lies_between_centroid_and_blind():
+    b, nb = 8, 24
+    q, k = rnd(70, 2, 4, b * nb, 6), rnd(71, 2, 2, b * nb, 6)
+    for alpha in (0.0, 0.5, 1.0):
+        aware = M.build_mask(q, k, 0.5, b, 150, alpha, rescue_mode=1)
+        blind = M.build_mask(q, k, 0.5, b, 150, alpha, rescue_mode=0)
+        floor = M.build_mask(q, k, 0.5, b, 150, math.inf, rescue_mode=1)
+        assert (aware.mask <= blind.mask).all() and (floor.mask <= aware.mask).all()
+        np.testing.assert_array_equal(floor.mask, M.build_mask(q, k, 0.5, b, 150, math.inf).mask)
+        assert (aware.rescued <= blind.rescued).all()
+        # the coefficient is in [0, 1], so the allowance never exceeds the Cauchy-Schwarz bound
+        assert ((aware.lam >= 0) & (aware.lam <= 1)).all()
+    # equal radii: nothing is a candidate and the modes agree with the centroid branch
+    kk = np.zeros((1, 1, b * nb, 6))
+    kk[0, 0, ::b, 0] = 1.0                                         # every block: one key at e0, radius (b-1)/b
+    qq = rnd(72, 1, 2, b * nb, 6)
+    eq = M.build_mask(qq, kk, 0.5, b, 150, 0.0, rescue_mode=1)
+    assert eq.lam[0, 0] == 0.0 and not eq.rescued.any()
+
+
+def test_query_aware_rescue_keeps_every_planted_block():
+    """The planted keys sit in the direction of one query row, so their block's excess radius earns an allowance
+    far above the centroid cutoff of the row that holds that query; mode 1 keeps every planted block there while
+    rescuing fewer blocks overall than the query-blind rule."""
+    inp = W.planted_inputs(3, 1, 8, 2, 64 * 64, 64, block=64, planted_per_mille=100)
+    q, k, _ = inp.as_f64()
+    aware = M.build_mask(q, k, inp.scale, 64, keep_permille=100, alpha=1.0, rescue_mode=1)
+    blind = M.build_mask(q, k, inp.scale, 64, keep_permille=100, alpha=1.0, rescue_mode=0)
+    for (b, g, j, u, h, t) in inp.planted:
+        assert aware.mask[b, h, t // 64, j] == 1
+    assert aware.mask.sum() < blind.mask.sum()
