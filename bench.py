@@ -8,7 +8,8 @@ A step runs every variant once, each on its own synthetic workload, with inputs 
   decode  split-KV paged decode, B32 Hq64 Hkv8 D64, lengths U[1024, 32768], page 16, 512-token chunks
 `value` is the dense prefill's TFLOP/s (causal count 2*B*Hq*N^2*D over the kernel's own event-timed duration).
 After the timed steps the long-context lines are measured on their own: dense prefill at 32K and 128K and the
-128K mask + sparse pass (speedup over this build's dense kernel at the same length). The fp64 CPU oracle is timed
+128K mask + sparse pass (speedup over this build's dense kernel at the same length), and at 32K and 128K the mask
+built with the query-aware rescue (rescue_mode 1) and the sparse pass over it. The fp64 CPU oracle is timed
 on the host (cpu_baseline) on the headline workload. One JSON line goes to stdout.
 """
 from __future__ import annotations
@@ -225,6 +226,32 @@ def main():
         x = [a.elapsed_time(b) for a, b in es]
         return float(np.mean(x)), spread(x)
 
+    def planted_kept(mask, planted, block):
+        """How many planted key blocks the mask keeps in the row of the query they were planted for."""
+        if not planted:
+            return None
+        idx = torch.tensor([[b, h, t // block, j] for (b, g, j, u, h, t) in planted], device=mask.device).T
+        return {"kept": int(mask[idx[0], idx[1], idx[2], idx[3]].sum().item()), "planted": len(planted)}
+
+    def query_aware(q, k, v, o, w, scale, t_dense_same_n, planted, reps):
+        """Mask build with the query-aware rescue (rescue_mode 1) and the sparse pass over its lists."""
+        blk, nbq = w["block"], w["N"] // w["block"]
+        mk = lambda out=None: lca.block_mask_build(q, k, blk, w["keep_permille"], w["alpha"], w["q_lo_pct"],
+                                                   w["q_hi_pct"], scale=scale, want_radius_stats=False,
+                                                   outputs=out, rescue_mode=1)
+        m = mk()
+        tm, stm = time_calls(lambda: mk(m), reps)
+        ts, sts = time_calls(lambda: lca.prefill_block_sparse(q, k, v, m.kv_count, m.kv_index, blk, scale=scale,
+                                                              out=o, return_lse=False), reps)
+        cnt = m.kv_count.cpu().numpy().astype(np.int64)
+        ex = float(((cnt - 1) * 4.0 * blk * blk * w["D"] + 2.0 * blk * (blk + 1) * w["D"]).sum())
+        return {"mask_ms": tm, "mask_ms_median": stm["ms_median"], "sparse_ms": ts, "sparse_ms_median": sts["ms_median"],
+                "density": float(cnt.sum() / (w["Hq"] * nbq * (nbq + 1) / 2)),
+                "executed_tflops": ex / (ts * 1e-3) / 1e12,
+                "speedup_vs_dense_kernel_only": t_dense_same_n / ts,
+                "speedup_vs_dense_incl_mask": t_dense_same_n / (ts + tm),
+                "planted_kept": planted_kept(m.mask, planted, blk)}
+
     if not args.no_long:
         log("dense prefill at 32K")
         t32, s32 = time_calls(lambda: lca.prefill_dense(q3, k3, v3, scale=c3.scale, out=o3, return_lse=False),
@@ -233,6 +260,10 @@ def main():
         paths["dense_prefill_n32768"] = {"ms": t32, **s32, "tflops": tf32, "pct_bf16_peak": 100 * tf32 / PEAK_BF16_TFLOPS}
         paths["sparse_prefill_n32768_b64"]["speedup_vs_dense_kernel_only"] = t32 / t_sparse3
         paths["sparse_prefill_n32768_b64"]["speedup_vs_dense_incl_mask"] = t32 / (t_sparse3 + t_mask3)
+        paths["sparse_prefill_n32768_b64"]["planted_kept"] = planted_kept(m3.mask, c3.planted, w3["block"])
+        log("query-aware rescue at 32K")
+        paths["sparse_prefill_n32768_b64"]["query_aware_rescue"] = query_aware(
+            q3, k3, v3, o3, w3, c3.scale, t32, c3.planted, max(args.long_reps, 5))
         del q3, k3, v3, o3, m3
         torch.cuda.empty_cache()
         log("generating the 128K block-sparse workload")
@@ -240,6 +271,7 @@ def main():
         c4 = W.make("c4_sparse_bf16_n128k")
         q4, k4, v4 = to_dev(c4.q), to_dev(c4.k), to_dev(c4.v)
         o4 = torch.empty_like(q4)
+        planted4 = c4.planted
         del c4
         log("dense prefill at 128K")
         t128, s128 = time_calls(lambda: lca.prefill_dense(q4, k4, v4, scale=1 / math.sqrt(128), out=o4,
@@ -267,8 +299,13 @@ def main():
             "pct_bf16_peak_executed": 100 * exec4 / (ts4 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "dense_equiv_tflops_incl_mask": fl128 / ((ts4 + tm4) * 1e-3) / 1e12,
             "speedup_vs_dense_kernel_only": t128 / ts4,
-            "speedup_vs_dense_incl_mask": t128 / (ts4 + tm4)}
-        del q4, k4, v4, o4, m4
+            "speedup_vs_dense_incl_mask": t128 / (ts4 + tm4),
+            "planted_kept": planted_kept(m4.mask, planted4, b4)}
+        del m4
+        log("query-aware rescue at 128K")
+        paths["sparse_prefill_n131072_b128"]["query_aware_rescue"] = query_aware(
+            q4, k4, v4, o4, w4, 1 / math.sqrt(128), t128, planted4, args.long_reps)
+        del q4, k4, v4, o4
         torch.cuda.empty_cache()
 
     cpu = None

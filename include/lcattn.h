@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define LCATTN_ABI_VERSION 1
+#define LCATTN_ABI_VERSION 2
 
 typedef enum {
     ATTN_OK = 0,
@@ -63,6 +63,7 @@ typedef struct {
     double rescue_alpha;   /* tau = med + alpha * (p_hi - med); +INF disables the rescue branch, >= 0       */
     int32_t q_lo_pct;      /* lower reference percentile of the radii (50 = median), 0..100                */
     int32_t q_hi_pct;      /* upper reference percentile (90), q_lo_pct <= q_hi_pct <= 100                 */
+    int32_t rescue_mode;   /* 0: a flagged block is rescued for every row; 1: query-aware (step 4b), 0 or 1 */
 } attn_mask_params_t;
 
 /* Decode problem: q [batch, heads_q, head_dim]; caches [num_pages, heads_kv, page_size, head_dim];
@@ -97,8 +98,13 @@ size_t attn_block_mask_workspace_bytes(const attn_shape_t* shape, const attn_mas
  *      tau = med + alpha * (p_hi - med);
  *   3. rescue flag of key block j: radius_j > tau (strict), shared by the kv head's query heads;
  *   4. centroid branch of row (h, i): among key blocks j <= i, the ceil((i+1) * keep_permille / 1000) largest
- *      scale * <query-block mean, key centroid> (float64), ties to the smaller j;
- *   5. mask[h,i,j] = 1 iff j <= i and (centroid pick or rescue flag or j == i).
+ *      S_ij = scale * <query-block mean, key centroid> (float64), ties to the smaller j;
+ *   4b. rescue_mode 0: every flagged j <= i is rescued in row (h, i). rescue_mode 1 (query-aware; the section's
+ *      coefficient from the median and the upper percentile, candidates scored against the base path): with
+ *      lambda = (p_hi - med) / p_hi (0 if p_hi == 0) and cut_i the smallest score the centroid branch kept in the
+ *      row, a flagged j is rescued in row (h, i) only if S_ij + lambda * scale * |query-block mean| * (radius_j -
+ *      med) > cut_i (no rescue when the row keeps no centroid pick);
+ *   5. mask[h,i,j] = 1 iff j <= i and (centroid pick or rescued or j == i).
  * Inputs: q, k bf16 in the prefill layouts. Outputs:
  *   mask      uint8 [batch, heads_q, nb, nb], 0/1, written in full.
  *   kv_count  int32 [batch, heads_q, nb], number of kept blocks per row.
@@ -107,7 +113,7 @@ size_t attn_block_mask_workspace_bytes(const attn_shape_t* shape, const attn_mas
  *   radius_stats  optional float64 [batch, heads_kv, nb + 3]: the nb radii, then med, p_hi, tau (NULL to skip).
  * Workspace (>= attn_block_mask_workspace_bytes, 256-byte aligned) holds, in order and each 256-byte aligned:
  * query-block means f64 [batch, heads_q, nb, head_dim], key centroids f64 [batch, heads_kv, nb, head_dim],
- * radii f64 [batch, heads_kv, nb], (med, p_hi, tau, 0) f64 [batch, heads_kv, 4], rescue flags u8
+ * radii f64 [batch, heads_kv, nb], (med, p_hi, tau, lambda) f64 [batch, heads_kv, 4], rescue flags u8
  * [batch, heads_kv, nb], centroid scores f64 [batch, heads_q, nb, nb] (lower triangle only).
  * Supported: bf16, head_dim 64 or 128, block_size a multiple of 64 dividing seq_len, 1 <= nb <= 4096.
  */

@@ -42,7 +42,8 @@ class AttnShape(ctypes.Structure):
 
 class AttnMaskParams(ctypes.Structure):
     _fields_ = [("block_size", ctypes.c_int32), ("keep_permille", ctypes.c_int32),
-                ("rescue_alpha", ctypes.c_double), ("q_lo_pct", ctypes.c_int32), ("q_hi_pct", ctypes.c_int32)]
+                ("rescue_alpha", ctypes.c_double), ("q_lo_pct", ctypes.c_int32), ("q_hi_pct", ctypes.c_int32),
+                ("rescue_mode", ctypes.c_int32)]
 
 
 class AttnDecodeShape(ctypes.Structure):
@@ -185,20 +186,22 @@ class BlockMask:
 
 def block_mask_workspace_bytes(q: torch.Tensor, k: torch.Tensor, block_size: int, keep_permille: int,
                                rescue_alpha: float, q_lo_pct: int = 50, q_hi_pct: int = 90,
-                               scale: Optional[float] = None) -> int:
+                               scale: Optional[float] = None, rescue_mode: int = 0) -> int:
     shp = _prefill_shape(q, k, k, scale)
-    prm = AttnMaskParams(block_size, keep_permille, float(rescue_alpha), q_lo_pct, q_hi_pct)
+    prm = AttnMaskParams(block_size, keep_permille, float(rescue_alpha), q_lo_pct, q_hi_pct, rescue_mode)
     return int(load().attn_block_mask_workspace_bytes(ctypes.byref(shp), ctypes.byref(prm)))
 
 
 def block_mask_build(q: torch.Tensor, k: torch.Tensor, block_size: int, keep_permille: int, rescue_alpha: float,
                      q_lo_pct: int = 50, q_hi_pct: int = 90, scale: Optional[float] = None,
                      want_radius_stats: bool = True, workspace: Optional[torch.Tensor] = None,
-                     outputs: Optional[BlockMask] = None, stream=None) -> BlockMask:
-    """The centroid + radius-rescue block mask (bf16 q/k). Returns the mask, CSR lists and optional stats."""
+                     outputs: Optional[BlockMask] = None, stream=None, rescue_mode: int = 0) -> BlockMask:
+    """The centroid + radius-rescue block mask (bf16 q/k). Returns the mask, CSR lists and optional stats.
+    rescue_mode 0 rescues a flagged block in every row; 1 keeps it only in rows whose centroid cutoff its
+    score plus the radius allowance beats."""
     lib = load()
     shp = _prefill_shape(q, k, k, scale)
-    prm = AttnMaskParams(block_size, keep_permille, float(rescue_alpha), q_lo_pct, q_hi_pct)
+    prm = AttnMaskParams(block_size, keep_permille, float(rescue_alpha), q_lo_pct, q_hi_pct, rescue_mode)
     need = int(lib.attn_block_mask_workspace_bytes(ctypes.byref(shp), ctypes.byref(prm)))
     if need == 0:   # the library rejects these parameters; this call reports why
         _check(lib.attn_block_mask_build(ctypes.byref(shp), ctypes.byref(prm), _ptr(q), _ptr(k), None, None, None,

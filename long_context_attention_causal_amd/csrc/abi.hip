@@ -89,6 +89,7 @@ attn_status_t check_mask_params(const attn_shape_t* s, const attn_mask_params_t*
     if (std::isnan(m->rescue_alpha) || m->rescue_alpha < 0.0) return fail(ATTN_ERR_SHAPE, "rescue_alpha must be >= 0");
     if (m->q_lo_pct < 0 || m->q_hi_pct > 100 || m->q_lo_pct > m->q_hi_pct)
         return fail(ATTN_ERR_SHAPE, "need 0 <= q_lo_pct <= q_hi_pct <= 100");
+    if (m->rescue_mode != 0 && m->rescue_mode != 1) return fail(ATTN_ERR_SHAPE, "rescue_mode must be 0 or 1");
     return ATTN_OK;
 }
 
@@ -186,6 +187,7 @@ attn_status_t attn_block_mask_build(const attn_shape_t* shape, const attn_mask_p
     p.alpha = params->rescue_alpha;
     p.lo_pct = params->q_lo_pct;
     p.hi_pct = params->q_hi_pct;
+    p.rescue_mode = params->rescue_mode;
     p.mask = mask;
     p.kv_count = kv_count;
     p.kv_index = kv_index;

@@ -31,6 +31,7 @@ struct MaskProblem {
     int keep_permille;
     double alpha;
     int lo_pct, hi_pct;
+    int rescue_mode;       // 0 query-blind, 1 query-aware
     uint8_t* mask;
     int32_t* kv_count;
     int32_t* kv_index;

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(1024) void mask_threshold_kernel(const ThreshArgs a
         t[0] = med;
         t[1] = hi;
         t[2] = tau;
-        t[3] = 0.0;
+        t[3] = hi == 0.0 ? 0.0 : (hi - med) / hi;   // query-aware rescue coefficient
         if (a.radius_stats) {
             double* rsd = a.radius_stats + (size_t)bg * (n + 3);
             rsd[n] = med;
@@ -283,10 +283,14 @@ __global__ __launch_bounds__(256) void mask_scores_kernel(const ScoreArgs a) {
 struct SelectArgs {
     const double* scores;
     const uint8_t* flags;
+    const double* qbar;    // query-aware mode: [B*Hq*nb][D]
+    const double* radius;  // query-aware mode: [B*Hkv][nb]
+    const double* thresh;  // query-aware mode: [B*Hkv][4] = (med, p_hi, tau, lambda)
     uint8_t* mask;
     int32_t* kv_count;
     int32_t* kv_index;
-    int B, Hq, Hkv, G, nb, keep;
+    int B, Hq, Hkv, G, nb, keep, D, mode;
+    double scale;
 };
 
 // Order-preserving map of a double onto uint64 (after folding -0 onto +0, which compares equal).
@@ -360,6 +364,31 @@ __global__ __launch_bounds__(256) void mask_select_kernel(const SelectArgs a) {
             }
         }
     }
+    // Query-aware rescue: a flagged block j stays a rescue only where its centroid score plus the allowance
+    // lambda * scale * |qbar_i| * (r_j - med) beats this row's centroid cutoff (the smallest kept score). When the
+    // budget covers every candidate the row is full anyway; with no budget there is no cutoff to beat.
+    const bool aware = a.mode == 1 && budget < cand;
+    double cut = INFINITY, coef = 0.0, med = 0.0;
+    const double* rad = nullptr;
+    if (aware) {
+#pragma clang fp contract(off)
+        if (budget > 0) {
+            uint64_t lo = ~0ull;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (kept[e]) lo = min(lo, key[e]);
+            for (int o = 32; o >= 1; o >>= 1) lo = min(lo, (uint64_t)__shfl_xor((unsigned long long)lo, o));
+            cut = __longlong_as_double((long long)((lo >> 63) ? (lo & 0x7fffffffffffffffull) : ~lo));
+        }
+        const double* qr = a.qbar + (size_t)row * a.D;
+        double ss = 0.0;
+        for (int d = lane; d < a.D; d += 64) ss += qr[d] * qr[d];
+        for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+        const double* th = a.thresh + ((size_t)b * a.Hkv + g) * 4;
+        med = th[0];
+        coef = th[3] * a.scale * sqrt(ss);
+        rad = a.radius + ((size_t)b * a.Hkv + g) * a.nb;
+    }
     uint8_t* mrow = a.mask + (size_t)row * a.nb;
     int32_t* irow = a.kv_index + (size_t)row * a.nb;
     const uint64_t below = (1ull << lane) - 1ull;
@@ -367,7 +396,12 @@ __global__ __launch_bounds__(256) void mask_select_kernel(const SelectArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int j = lane + 64 * e;
-        const bool m = j <= i && (kept[e] || fl[j] != 0 || j == i);
+        bool resc = j <= i && fl[j] != 0;
+        if (aware && resc && !kept[e]) {
+#pragma clang fp contract(off)
+            resc = srow[j] + coef * (rad[j] - med) > cut;
+        }
+        const bool m = j <= i && (kept[e] || resc || j == i);
         if (j < a.nb) mrow[j] = m ? 1 : 0;
         const uint64_t bal = __ballot(m);
         if (m) irow[count + __popcll(bal & below)] = j;
@@ -457,6 +491,12 @@ hipError_t launch_block_mask(const MaskProblem& p, const MaskWorkspace& ws, hipS
     se.G = p.Hq / p.Hkv;
     se.nb = p.nb;
     se.keep = p.keep_permille;
+    se.qbar = ws.qbar;
+    se.radius = ws.radius;
+    se.thresh = ws.thresh;
+    se.D = p.D;
+    se.mode = p.rescue_mode;
+    se.scale = p.scale;
     const long rows = (long)p.B * p.Hq * p.nb;
     const dim3 grid((unsigned)((rows + 3) / 4));
     const int E = (p.nb + 63) / 64;

@@ -38,7 +38,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert lca.abi_version() == 1
+    assert lca.abi_version() == 2
     for st in range(7):
         assert L.attn_status_string(st)
     assert L.attn_status_string(99) == b"unknown status"
@@ -74,8 +74,8 @@ def test_prefill_dense_pointer_checks(L):
     assert dense(L, shape(N=0), q=None) == 0      # empty problem: nothing to do, nothing read
 
 
-def params(block=64, keep=100, alpha=1.0, lo=50, hi=90):
-    return lca.AttnMaskParams(block, keep, alpha, lo, hi)
+def params(block=64, keep=100, alpha=1.0, lo=50, hi=90, mode=0):
+    return lca.AttnMaskParams(block, keep, alpha, lo, hi, mode)
 
 
 @pytest.mark.parametrize("s,p,code", [
@@ -87,6 +87,8 @@ def params(block=64, keep=100, alpha=1.0, lo=50, hi=90):
     (shape(), params(alpha=math.nan), 2),
     (shape(), params(lo=90, hi=50), 2),
     (shape(N=64 * 5000), params(), 3),
+    (shape(), params(mode=2), 2),
+    (shape(), params(mode=-1), 2),
 ])
 def test_mask_build_rejects(L, s, p, code):
     assert L.attn_block_mask_workspace_bytes(ctypes.byref(s), ctypes.byref(p)) == 0
@@ -99,6 +101,9 @@ def test_mask_workspace_size_and_check(L):
     nb = N // blk
     s, p = shape(B, Hq, Hkv, N, D), params(blk)
     need = L.attn_block_mask_workspace_bytes(ctypes.byref(s), ctypes.byref(p))
+    # the query-aware rescue reads only buffers the workspace already holds
+    assert L.attn_block_mask_workspace_bytes(ctypes.byref(s), ctypes.byref(params(blk, mode=1))) == need
+    assert ctypes.sizeof(lca.AttnMaskParams) == 32
     a = lambda x: (x + 255) // 256 * 256
     want = (a(B * Hq * nb * D * 8) + a(B * Hkv * nb * D * 8) + a(B * Hkv * nb * 8) + a(B * Hkv * 32)
             + a(B * Hkv * nb) + a(B * Hq * nb * nb * 8))

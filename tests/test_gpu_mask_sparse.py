@@ -14,18 +14,20 @@ from tests.gpu_util import BF16_TOL, LSE_TOL, dev_i32, host64, max_err, prefill_
 pytestmark = pytest.mark.gpu
 
 
-def gpu_mask(lib, inp, keep, alpha, lo=50, hi=90):
+def gpu_mask(lib, inp, keep, alpha, lo=50, hi=90, mode=0):
     q, k, _ = prefill_to_device(inp)
-    m = lib.block_mask_build(q, k, inp.block, keep, alpha, lo, hi, scale=inp.scale)
+    m = lib.block_mask_build(q, k, inp.block, keep, alpha, lo, hi, scale=inp.scale, rescue_mode=mode)
     torch.cuda.synchronize()
     return m
 
 
 def ambiguous_rows(ref: M.MaskResult, G: int) -> np.ndarray:
     """Rows whose result may legitimately differ between two correct fp64 evaluations: the centroid cut falls on
-    a score gap below 1e-12 relative, or a radius lies within 1e-12 relative of its threshold."""
-    amb = ref.cut_gap < 1e-12 * (1.0 + ref.score_absmax)
-    near = np.abs(ref.radius - ref.tau[:, :, None]) <= 1e-12 * np.abs(ref.tau[:, :, None])
+    a score gap below 1e-12 relative, a radius lies within 1e-12 relative of its threshold, or (query-aware
+    rescue) a candidate's rescue score lies within 1e-12 relative of the row's cutoff."""
+    amb = (ref.cut_gap < 1e-12 * (1.0 + ref.score_absmax)) | (ref.rescue_gap < 1e-12)
+    tau = ref.tau[:, :, None]
+    near = np.isfinite(tau) & (np.abs(ref.radius - tau) <= 1e-12 * np.abs(tau))   # tau = inf flags nothing
     B, Hq, nb = ref.kv_count.shape
     for h in range(Hq):
         touched = near[:, h // G, :]                      # [B, nb] key blocks
@@ -36,12 +38,13 @@ def ambiguous_rows(ref: M.MaskResult, G: int) -> np.ndarray:
     return amb
 
 
-def compare_mask(lib, inp, keep, alpha, label, lo=50, hi=90):
-    say(f"[mask] {label}: gpu")
-    m = gpu_mask(lib, inp, keep, alpha, lo, hi)
+def compare_mask(lib, inp, keep, alpha, label, lo=50, hi=90, mode=0):
+    say(f"[mask] {label} mode {mode}: gpu")
+    m = gpu_mask(lib, inp, keep, alpha, lo, hi, mode)
     q, k, _ = inp.as_f64()
-    say(f"[mask] {label}: oracle")
-    ref = M.build_mask(q, k, inp.scale, inp.block, keep, alpha, lo, hi)
+    say(f"[mask] {label} mode {mode}: oracle")
+    # the library takes the scale as float32
+    ref = M.build_mask(q, k, float(np.float32(inp.scale)), inp.block, keep, alpha, lo, hi, rescue_mode=mode)
     G = inp.q.shape[1] // inp.k.shape[1]
     mask = m.mask.cpu().numpy()
     cnt = m.kv_count.cpu().numpy()
@@ -78,9 +81,10 @@ def compare_mask(lib, inp, keep, alpha, label, lo=50, hi=90):
     (1, 2, 1, 64 * 3, 128, 64, 100, 2.0),
     (1, 4, 2, 256 * 9, 128, 256, 200, 1.0),
 ])
-def test_mask_small(lib, B, Hq, Hkv, N, D, block, keep, alpha):
+@pytest.mark.parametrize("mode", [0, 1])
+def test_mask_small(lib, B, Hq, Hkv, N, D, block, keep, alpha, mode):
     inp = W.planted_inputs(41, B, Hq, Hkv, N, D, block)
-    compare_mask(lib, inp, keep, alpha, f"small {B},{Hq},{Hkv},{N},{D},b{block},k{keep},a{alpha}")
+    compare_mask(lib, inp, keep, alpha, f"small {B},{Hq},{Hkv},{N},{D},b{block},k{keep},a{alpha}", mode=mode)
 
 
 def test_mask_special_rules(lib):
@@ -92,15 +96,27 @@ def test_mask_special_rules(lib):
     assert (diag == np.eye(nb, dtype=np.uint8)).all()
     compare_mask(lib, inp, 150, math.inf, "centroid only")
     compare_mask(lib, inp, 0, 0.0, "rescue only, alpha 0")
+    # query-aware: alpha = inf is the centroid branch alone; no budget means no cutoff, so nothing is rescued
+    cen = compare_mask(lib, inp, 150, math.inf, "centroid only", mode=1)[0].mask.cpu().numpy()
+    assert (cen == gpu_mask(lib, inp, 150, math.inf).mask.cpu().numpy()).all()
+    diag1 = gpu_mask(lib, inp, 0, 0.0, mode=1).mask.cpu().numpy()
+    assert (diag1 == np.eye(nb, dtype=np.uint8)).all()
+    # alpha = 0 widens the candidates to every block above the median radius; the query-aware mask stays inside
+    # the query-blind one
+    aware, _ = compare_mask(lib, inp, 150, 0.0, "alpha 0", mode=1)
+    blind = gpu_mask(lib, inp, 150, 0.0).mask.cpu().numpy()
+    assert (aware.mask.cpu().numpy() <= blind).all()
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("name", ["c3_sparse_bf16_n32k", "c4_sparse_bf16_n128k"])
-def test_mask_full_size(lib, name):
+def test_mask_full_size(lib, name, mode):
     w = W.WORKLOADS[name]
     say(f"[mask] {name}: generating inputs")
     inp = W.planted_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["block"])
-    m, ref = compare_mask(lib, inp, w["keep_permille"], w["alpha"], name, w["q_lo_pct"], w["q_hi_pct"])
-    # every planted block is caught by the rescue branch (mean dilution would hide many from the centroids)
+    m, ref = compare_mask(lib, inp, w["keep_permille"], w["alpha"], name, w["q_lo_pct"], w["q_hi_pct"], mode)
+    # every planted block is kept in the row of the query it was planted for (mean dilution would hide many from
+    # the centroids; the query-aware rescue still reaches them through the radius allowance)
     mask = m.mask.cpu().numpy()
     for (b, g, j, u, h, t) in inp.planted:
         assert mask[b, h, t // w["block"], j] == 1
