@@ -123,6 +123,52 @@ def gather_paged(cache: np.ndarray, block_table: np.ndarray, b: int, length: int
     return cache[pid, :, t % page, :]
 
 
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """Values of 8-bit E4M3 codes as float64, per the OCP 8-bit floating point specification (OFP8): sign bit,
+    4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the subnormals M/8 * 2^-6; there are no
+    infinities and S.1111.111 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448. The pages ask for an
+    fp8 KV cache ("Your Context Length Decides What a Kernel Is Worth": moving fewer bytes through the
+    --kv-cache-dtype fp8 setting) without naming the encoding; E4M3 is read as that encoding."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def paged_decode_fp8(q: np.ndarray, k_codes: np.ndarray, v_codes_t: np.ndarray, k_scale: float, v_scale: float,
+                     block_table: np.ndarray, seq_lens: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Single-token decode over an fp8 paged cache: the keys and values are the E4M3 code values times one
+    scale per tensor, and the attention is then paged_decode's.
+
+    k_codes [num_pages, Hkv, page, D] (token-major, as the bf16 cache); v_codes_t [num_pages, Hkv, D, page]: the
+    value cache holds each page transposed, the page's tokens contiguous for every head dimension. Only the
+    tokens a sequence reaches are dequantised, so codes past its end (NaN included) play no part."""
+    B, Hq, D = q.shape
+    Hkv = k_codes.shape[1]
+    page = k_codes.shape[2]
+    G = _group(Hq, Hkv)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    lse = np.full((B, Hq), -np.inf, dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        t = np.arange(L)
+        pid, slot = block_table[b, t // page], t % page
+        K = e4m3_value(k_codes[pid, :, slot, :]) * float(k_scale)      # [L, Hkv, D]
+        V = e4m3_value(v_codes_t[pid, :, :, slot]) * float(v_scale)    # [L, Hkv, D]
+        for h in range(Hq):
+            g = h // G
+            s = scale * (K[:, g, :] @ q[b, h])
+            o, l = _softmax_rows(s[None, :], np.ones((1, L), dtype=bool), V[:, g, :])
+            out[b, h] = o[0]
+            lse[b, h] = l[0]
+    return out, lse
+
+
 def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray,
                  seq_lens: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
     """Single-token decode over a paged cache, unsplit.

@@ -99,3 +99,69 @@ def test_decode_intensity_matches_the_page():
     ai = flops_per_token / bytes_per_token
     assert ai == G
     assert abs(ai - gold["arithmetic_intensity_flop_per_byte"]) <= gold["tolerance"]
+
+
+# ------------------------------------------------------------------------------------------------- fp8 KV cache
+def test_e4m3_values_follow_the_format_definition():
+    """Anchors from the OFP8 E4M3 definition (bias 7, 3 mantissa bits, subnormals, NaN only at S.1111.111) and the
+    whole code table against PyTorch's float8_e4m3fn, an independent implementation of the same format."""
+    import torch
+    anchors = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+               0x40: 2.0, 0xC0: -2.0, 0x7E: 448.0, 0xFE: -448.0, 0x77: 240.0, 0x80: 0.0}
+    for c, v in anchors.items():
+        assert A.e4m3_value(np.array([c]))[0] == v, hex(c)
+    assert np.isnan(A.e4m3_value(np.array([0x7F, 0xFF]))).all()
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    mine = A.e4m3_value(codes)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+
+
+def test_e4m3_encoder_rounds_to_nearest_even_and_saturates():
+    """The generator's encoder against PyTorch's float8_e4m3fn conversion (round to nearest even) on random
+    values over the whole range, exact midpoints and the subnormal range; beyond 448 it saturates."""
+    import torch
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000) * 64, rng.standard_normal(5000) * 2.0 ** -7,
+                        (np.arange(-40, 40) + 0.5) * 2.0 ** -9, np.array([1.0625, 1.1875, 17.0, 19.0, 0.0]),
+                        rng.uniform(-448, 448, 5000)]).astype(np.float32)
+    mine = W.e4m3_codes_from_f32(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+    assert W.e4m3_codes_from_f32(np.array([1000.0, -500.0], np.float32)).tolist() == [0x7E, 0xFE]
+
+
+def test_fp8_decode_is_decode_over_the_dequantised_cache():
+    """Every E4M3 value times a power-of-two scale is a bf16 number, so decoding the fp8 cache must equal the bf16
+    oracle decoding a cache that holds those numbers (with V transposed back to token-major)."""
+    d = W.decode_inputs_fp8(7, 4, 8, 2, 16, 16, 1, 200, k_scale=2.0 ** -5, v_scale=2.0 ** -7,
+                            seq_lens=np.array([1, 16, 33, 200], np.int32))
+    q = W.f64_from_bf16_bits(d.q)
+    O8, L8 = A.paged_decode_fp8(q, d.k_cache, d.v_cache_t, d.k_scale, d.v_scale, d.block_table, d.seq_lens, d.scale)
+    kf = np.nan_to_num(A.e4m3_value(d.k_cache)) * d.k_scale
+    vf = np.nan_to_num(A.e4m3_value(d.v_cache_t.transpose(0, 1, 3, 2))) * d.v_scale
+    O, L = A.paged_decode(q, kf, vf, d.block_table, d.seq_lens, d.scale)
+    assert np.isfinite(O8).all()
+    np.testing.assert_array_equal(O8, O)
+    np.testing.assert_array_equal(L8, L)
+
+
+def test_fp8_needle_reads_the_transposed_value_page():
+    """One sequence of 20 tokens over two pages, head_dim 4. Keys are zero except token 17, whose key makes its
+    score 448 * 2 * scale larger than every other; the output is then token 17's value row, which sits in page
+    table[1], slot 1, spread over the page's head-dim rows: V^T[page][g][d][1]. Codes: 0x38 = 1, 0x40 = 2,
+    0x48 = 4, 0x30 = 0.5. With v_scale 2 the value row is (2, 4, 8, 1)."""
+    D, page, Hkv = 4, 16, 1
+    bt = np.array([[3, 0]], np.int32)
+    kc = np.zeros((4, Hkv, page, D), np.uint8)
+    vt = np.full((4, Hkv, D, page), 0x38, np.uint8)     # every other value 1.0
+    kc[0, 0, 1, :] = 0x7E                                # token 17 = page bt[0,1] = 0, slot 1: key 448 * (1,1,1,1)
+    vt[0, 0, :, 1] = [0x38, 0x40, 0x48, 0x30]
+    kc[0, 0, 4:, :] = 0x7F                               # NaN past the end (tokens 20..31)
+    vt[0, 0, :, 4:] = 0x7F
+    q = np.full((1, 1, D), 1.0)
+    O, L = A.paged_decode_fp8(q, kc, vt, 1.0, 2.0, bt, np.array([20], np.int32), 1.0)
+    np.testing.assert_allclose(O[0, 0], [2.0, 4.0, 8.0, 1.0], atol=1e-300)
+    assert abs(L[0, 0] - 4 * 448.0) < 1e-9

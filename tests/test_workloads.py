@@ -68,3 +68,30 @@ def test_sample_rows_hold_the_fixed_rows():
         assert len(r) == rows.shape[1]
     for (b, g, j, u, h, t) in inp.planted:
         assert t in set(rows[h].tolist())
+
+
+def test_fp8_decode_inputs_match_the_bf16_workload():
+    """Same lengths, block table and activation draws as the bf16 decode workload; codes are the E4M3 rounding of
+    value / scale (within half a quantum of the bf16 values), the value cache is transposed within each page, and
+    slots past each sequence hold the NaN code."""
+    import torch
+    d = W.decode_inputs(9, 3, 8, 2, 16, 16, 1, 100)
+    f = W.decode_inputs_fp8(9, 3, 8, 2, 16, 16, 1, 100, k_scale=2.0 ** -6, v_scale=2.0 ** -6)
+    assert np.array_equal(d.seq_lens, f.seq_lens) and np.array_equal(d.block_table, f.block_table)
+    assert np.array_equal(d.q, f.q)
+    assert f.v_cache_t.shape == (f.k_cache.shape[0], 2, 16, 16)
+    kv = torch.from_numpy(f.k_cache).view(torch.float8_e4m3fn).double().numpy() * f.k_scale
+    vv = torch.from_numpy(np.ascontiguousarray(f.v_cache_t.transpose(0, 1, 3, 2))).view(
+        torch.float8_e4m3fn).double().numpy() * f.v_scale
+    kb, vb = W.f64_from_bf16_bits(d.k_cache), W.f64_from_bf16_bits(d.v_cache)
+    for b in range(3):
+        L = int(d.seq_lens[b])
+        t = np.arange(L)
+        pid, slot = d.block_table[b, t // 16], t % 16
+        for a, ref in ((kv, kb), (vv, vb)):
+            x, y = a[pid, :, slot, :], ref[pid, :, slot, :]
+            # E4M3 keeps 3 mantissa bits: relative error <= 2^-4 (normal range); bf16 adds 2^-8 more
+            assert np.all(np.abs(x - y) <= np.abs(y) * (2.0 ** -4 + 2.0 ** -8) + 2.0 ** -10 * f.k_scale)
+        if L % 16:
+            assert (f.k_cache[d.block_table[b, L // 16], :, L % 16:, :] == 0x7F).all()
+            assert (f.v_cache_t[d.block_table[b, L // 16], :, :, L % 16:] == 0x7F).all()

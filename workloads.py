@@ -50,6 +50,24 @@ def f64_from_bf16_bits(u: np.ndarray) -> np.ndarray:
     return f32_from_bf16_bits(u).astype(np.float64)
 
 
+def e4m3_codes_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to 8-bit E4M3 codes (OCP OFP8: bias 7, 3 mantissa bits, subnormals below 2^-6, largest
+    finite 448) with round-to-nearest-even, saturating at +-448; returns uint8 codes. Inputs are assumed finite."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    _, ex = np.frexp(a)                       # a = f * 2^ex with f in [0.5, 1): binade exponent ex - 1
+    e = np.maximum(ex.astype(np.int64) - 1, -6)
+    quantum = np.exp2((e - 3).astype(np.float64))
+    m = np.round(a / quantum).astype(np.int64)   # numpy rounds halves to even; a / quantum is exact
+    carry = m == 16
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 8, m)
+    sub = m < 8                               # only where e == -6: the subnormal range
+    code = np.where(sub, m, ((e + 7) << 3) | (m - 8))
+    code = np.where(x < 0, code | 0x80, code)
+    return code.astype(np.uint8)
+
+
 def streams(seed: int, names: List[str]) -> Dict[str, np.random.Generator]:
     """Independent PCG64 generators, one per purpose, spawned from one SeedSequence."""
     children = np.random.SeedSequence(seed).spawn(len(names))
@@ -199,6 +217,75 @@ def decode_inputs(seed: int, B: int, Hq: int, Hkv: int, D: int, page: int, len_l
                         scale=float(1.0 / np.sqrt(D)))
 
 
+@dataclass
+class DecodeInputsFP8:
+    """q [B,Hq,D] bf16 bits; k_cache [num_pages,Hkv,page,D] and v_cache_t [num_pages,Hkv,D,page] E4M3 codes
+    (uint8; the value cache holds each page transposed); one scale per cache; block_table, seq_lens as in
+    DecodeInputs. Slots at or past seq_lens[b] in a sequence's last page hold the NaN code 0x7F."""
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache_t: np.ndarray
+    k_scale: float
+    v_scale: float
+    block_table: np.ndarray
+    seq_lens: np.ndarray
+    page: int
+    scale: float
+
+
+E4M3_NAN_CODE = np.uint8(0x7F)
+
+
+def _normal_e4m3(rng: np.random.Generator, shape: Tuple[int, ...], inv_scale: float,
+                 chunk_elems: int = 1 << 26) -> np.ndarray:
+    """i.i.d. N(0,1) fp32 draws (the same draws as _normal_bf16 on the same stream) times inv_scale, rounded to
+    E4M3 codes."""
+    total = int(np.prod(shape))
+    out = np.empty(total, dtype=np.uint8)
+    for s in range(0, total, chunk_elems):
+        e = min(total, s + chunk_elems)
+        out[s:e] = e4m3_codes_from_f32(rng.standard_normal(e - s, dtype=np.float32) * np.float32(inv_scale))
+    return out.reshape(shape)
+
+
+def decode_inputs_fp8(seed: int, B: int, Hq: int, Hkv: int, D: int, page: int, len_lo: int, len_hi: int,
+                      k_scale: float = 2.0 ** -6, v_scale: float = 2.0 ** -6, poison_tail: bool = True,
+                      seq_lens: Optional[np.ndarray] = None) -> DecodeInputsFP8:
+    """The paged decode workload of decode_inputs (same lengths, page permutation, block table and activation
+    draws) with K and V stored as E4M3 codes of value / scale, one scale per cache. The default scale 2^-6 maps
+    the N(0,1) activations onto the format's range (7 sigma saturates at 448) and is exact to apply. The value
+    cache is written transposed within each page: [page id, kv head, head dim, slot]."""
+    r = streams(seed, ["q", "k", "v", "lens", "perm", "rows"])
+    if seq_lens is None:
+        lens = r["lens"].integers(len_lo, len_hi, size=B, endpoint=True).astype(np.int32)
+    else:
+        lens = np.asarray(seq_lens, dtype=np.int32)
+    pages_per = (lens.astype(np.int64) + page - 1) // page
+    num_pages = int(pages_per.sum())
+    max_pages = max(1, -(-int(len_hi) // page))
+    perm = r["perm"].permutation(num_pages).astype(np.int32)
+    bt = np.full((B, max_pages), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        n = int(pages_per[b])
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    P = max(num_pages, 1)
+    kc = _normal_e4m3(r["k"], (P, Hkv, page, D), 1.0 / k_scale)
+    vc = _normal_e4m3(r["v"], (P, Hkv, page, D), 1.0 / v_scale)
+    if poison_tail:
+        for b in range(B):
+            L = int(lens[b])
+            if L % page:
+                pid = bt[b, L // page]
+                kc[pid, :, L % page:, :] = E4M3_NAN_CODE
+                vc[pid, :, L % page:, :] = E4M3_NAN_CODE
+    vt = np.ascontiguousarray(vc.transpose(0, 1, 3, 2))
+    q = _normal_bf16(r["q"], (B, Hq, D))
+    return DecodeInputsFP8(q=q, k_cache=kc, v_cache_t=vt, k_scale=float(k_scale), v_scale=float(v_scale),
+                           block_table=bt, seq_lens=lens, page=page, scale=float(1.0 / np.sqrt(D)))
+
+
 # --------------------------------------------------------------------------------------------------------------
 # sampled query rows for large configurations
 # --------------------------------------------------------------------------------------------------------------
@@ -254,6 +341,9 @@ WORKLOADS = {
                                  keep_permille=50, alpha=1.0, q_lo_pct=50, q_hi_pct=90),
     "c5_decode_paged_bf16": dict(kind="decode", seed=5, B=32, Hq=64, Hkv=8, D=64, page=16, len_lo=1024,
                                  len_hi=32768, chunk=512),
+    # the same decode workload over an E4M3 KV cache (per-tensor scales 2^-6)
+    "c5_decode_paged_fp8": dict(kind="decode_fp8", seed=5, B=32, Hq=64, Hkv=8, D=64, page=16, len_lo=1024,
+                                len_hi=32768, chunk=512, k_scale=2.0 ** -6, v_scale=2.0 ** -6),
 }
 
 
@@ -266,4 +356,7 @@ def make(name: str):
         return planted_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["block"])
     if w["kind"] == "decode":
         return decode_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["D"], w["page"], w["len_lo"], w["len_hi"])
+    if w["kind"] == "decode_fp8":
+        return decode_inputs_fp8(w["seed"], w["B"], w["Hq"], w["Hkv"], w["D"], w["page"], w["len_lo"], w["len_hi"],
+                                 w["k_scale"], w["v_scale"])
     raise KeyError(name)
