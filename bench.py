@@ -7,7 +7,8 @@ A step runs every variant once, each on its own synthetic workload, with inputs 
   sparse  block-mask build + block-sparse prefill, N32768 block 64, centroid budget 10%, rescue alpha 1
   decode  split-KV paged decode, B32 Hq64 Hkv8 D64, lengths U[1024, 32768], page 16, 512-token chunks
 `value` is the dense prefill's TFLOP/s (causal count 2*B*Hq*N^2*D over the kernel's own event-timed duration).
-After the timed steps the long-context lines are measured on their own: dense prefill at 32K and 128K and the
+After the timed steps the decode workload is also run over an fp8 (E4M3) copy of its cache, and the long-context
+lines are measured on their own: dense prefill at 32K and 128K and the
 128K mask + sparse pass (speedup over this build's dense kernel at the same length), and at 32K and 128K the mask
 built with the query-aware rescue (rescue_mode 1) and the sparse pass over it. The fp64 CPU oracle is timed
 on the host (cpu_baseline) on the headline workload. One JSON line goes to stdout.
@@ -61,7 +62,7 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the 32K/128K dense and 128K sparse lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--long-reps", type=int, default=3)
-    ap.add_argument("--only", choices=["dense", "dense32k", "sparse", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["dense", "dense32k", "sparse", "decode", "decode8", "copy"], default=None,
                     help="run one path alone (for profiler runs); prints a short JSON line with its mean time")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -168,6 +169,44 @@ def main():
     del junk
     torch.cuda.empty_cache()
 
+    # the same decode workload over the fp8 (E4M3) cache: back to back, then cold like the bf16 line
+    log("generating the fp8 paged decode workload")
+    c8 = W.make("c5_decode_paged_fp8")
+    q8 = to_dev(c8.q)
+    k8, v8 = torch.from_numpy(c8.k_cache).to(dev), torch.from_numpy(c8.v_cache_t).to(dev)
+    bt8, sl8 = torch.from_numpy(c8.block_table).to(dev), torch.from_numpy(c8.seq_lens).to(dev)
+    o8 = torch.empty_like(q8)
+    dec8 = lambda: lca.decode_paged_fp8(q8, k8, v8, c8.k_scale, c8.v_scale, bt8, sl8, maxlen5, w5["chunk"],
+                                        scale=c8.scale, out=o8, return_lse=False, workspace=ws5)
+    log("paged decode over the fp8 cache")
+    dec8()
+    torch.cuda.synchronize()
+    warm8 = []
+    for _ in range(args.steps + 30):
+        a_, b_ = ev(), ev()
+        a_.record()
+        dec8()
+        b_.record()
+        warm8.append((a_, b_))
+    junk = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cold8 = []
+    for i in range(args.steps + 2):
+        junk.sum()
+        a_, b_ = ev(), ev()
+        a_.record()
+        dec8()
+        b_.record()
+        if i >= 2:
+            cold8.append((a_, b_))
+    torch.cuda.synchronize()
+    warm8_ms = [a_.elapsed_time(b_) for a_, b_ in warm8]
+    cold8_ms = [a_.elapsed_time(b_) for a_, b_ in cold8]
+    L8 = c8.seq_lens.astype(np.int64)
+    dec8_bytes = float(L8.sum() * w5["Hkv"] * w5["D"] * 2 + w5["B"] * w5["Hq"] * w5["D"] * 2 * 2
+                       + ((L8 + 15) // 16).sum() * 4)
+    del junk, q8, k8, v8, bt8, sl8, o8, c8
+    torch.cuda.empty_cache()
+
     B, Hq, N, D = c2.q.shape
     fl2 = dense_flops(B, Hq, N, D)
     tflops2 = fl2 / (t_dense * 1e-3) / 1e12
@@ -211,6 +250,15 @@ def main():
                             "pct_hbm_peak": 100 * dec_gbs / PEAK_HBM_GBS, "tokens_per_s": B5 / (t_dec * 1e-3),
                             "tflops": 4.0 * D5 * Hq5 * float(L5.sum()) / (t_dec * 1e-3) / 1e12},
     }
+
+    t8 = float(np.mean(warm8_ms))
+    paths["decode_paged_c5_fp8"] = {
+        "ms": t8, **spread(warm8_ms), "algorithmic_bytes": dec8_bytes, "gbs": dec8_bytes / (t8 * 1e-3) / 1e9,
+        "pct_hbm_peak": 100 * dec8_bytes / (t8 * 1e-3) / 1e9 / PEAK_HBM_GBS, "tokens_per_s": w5["B"] / (t8 * 1e-3),
+        "cold_ms": float(np.mean(cold8_ms)), "cold_ms_median": float(np.median(cold8_ms)),
+        "cold_gbs": dec8_bytes / (float(np.mean(cold8_ms)) * 1e-3) / 1e9,
+        "cold_pct_hbm_peak": 100 * dec8_bytes / (float(np.mean(cold8_ms)) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "speedup_vs_bf16_cold": float(np.mean(cold_ms)) / float(np.mean(cold8_ms))}
 
     def time_calls(fn, reps):
         fn()
@@ -365,6 +413,16 @@ def run_only(args, lca, W, torch, np, to_dev, dev):
                                  scale=c.scale, outputs=m)
             lca.prefill_block_sparse(q, k, v, m.kv_count, m.kv_index, w["block"], scale=c.scale, out=o,
                                      return_lse=False)
+    elif args.only == "decode8":
+        w = W.WORKLOADS["c5_decode_paged_fp8"]
+        c = W.make("c5_decode_paged_fp8")
+        q = to_dev(c.q)
+        kc, vc = torch.from_numpy(c.k_cache).to(dev), torch.from_numpy(c.v_cache_t).to(dev)
+        bt, sl = torch.from_numpy(c.block_table).to(dev), torch.from_numpy(c.seq_lens).to(dev)
+        o = torch.empty_like(q)
+        ws = torch.empty(lca.decode_workspace_bytes(q, kc, bt, w["len_hi"], w["chunk"]), dtype=torch.uint8, device=dev)
+        fn = lambda: lca.decode_paged_fp8(q, kc, vc, c.k_scale, c.v_scale, bt, sl, w["len_hi"], w["chunk"],
+                                          scale=c.scale, out=o, return_lse=False, workspace=ws)
     else:
         w = W.WORKLOADS["c5_decode_paged_bf16"]
         c = W.make("c5_decode_paged_bf16")

@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define LCATTN_ABI_VERSION 2
+#define LCATTN_ABI_VERSION 3
 
 typedef enum {
     ATTN_OK = 0,
@@ -161,6 +161,23 @@ attn_status_t attn_decode_paged(const attn_decode_shape_t* shape, const void* q,
                                 const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                                 int32_t max_seq_len, void* o, float* lse, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/*
+ * attn_decode_paged over an fp8 KV cache, which halves the bytes a decode step moves ("Your Context Length
+ * Decides What a Kernel Is Worth": decode is bandwidth-bound and an fp8 KV cache is one of the two things that
+ * help). Codes are OCP E4M3 (bias 7, 3 mantissa bits, subnormals, NaN at S.1111.111); a cached key is
+ * code value * k_scale and a cached value code value * v_scale.
+ *   k_cache    E4M3 [num_pages, heads_kv, page_size, head_dim] (token-major, like the bf16 cache)
+ *   v_cache_t  E4M3 [num_pages, heads_kv, head_dim, page_size]: each page transposed, its tokens contiguous
+ *   k_scale, v_scale  finite and > 0.
+ * Everything else -- q, block table, lengths, output, lse, workspace (attn_decode_workspace_bytes), the trusted
+ * inputs, the handling of slots past a sequence's end (any byte, the NaN code included) -- is as in
+ * attn_decode_paged. The codes are widened to bf16 exactly and the arithmetic is the bf16 path's.
+ */
+attn_status_t attn_decode_paged_fp8(const attn_decode_shape_t* shape, const void* q, const uint8_t* k_cache,
+                                    const uint8_t* v_cache_t, float k_scale, float v_scale,
+                                    const int32_t* block_table, const int32_t* seq_lens, int32_t max_seq_len,
+                                    void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 const char* attn_status_string(attn_status_t status);
 const char* attn_last_error(void);

@@ -54,8 +54,8 @@ class AttnDecodeShape(ctypes.Structure):
 
 
 EXPORTS = ("attn_prefill_dense", "attn_block_mask_workspace_bytes", "attn_block_mask_build",
-           "attn_prefill_block_sparse", "attn_decode_workspace_bytes", "attn_decode_paged", "attn_status_string",
-           "attn_last_error", "attn_abi_version")
+           "attn_prefill_block_sparse", "attn_decode_workspace_bytes", "attn_decode_paged", "attn_decode_paged_fp8",
+           "attn_status_string", "attn_last_error", "attn_abi_version")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -95,6 +95,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(AttnDecodeShape), i32]
     lib.attn_decode_paged.restype = i32
     lib.attn_decode_paged.argtypes = [ctypes.POINTER(AttnDecodeShape), vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.attn_decode_paged_fp8.restype = i32
+    lib.attn_decode_paged_fp8.argtypes = [ctypes.POINTER(AttnDecodeShape), vp, vp, vp, ctypes.c_float,
+                                          ctypes.c_float, vp, vp, i32, vp, vp, vp, sz, vp]
     runtimes = _hip_runtimes_mapped()
     if len(runtimes) > 1:
         raise LcattnError(6, f"two HIP runtimes mapped in this process: {runtimes}")
@@ -298,4 +301,39 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     _check(lib.attn_decode_paged(ctypes.byref(shp), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                  _ptr(seq_lens), int(max_seq_len), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
                                  _stream(stream, q.device)))
+    return o, lse
+
+
+def decode_paged_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache_t: torch.Tensor, k_scale: float,
+                     v_scale: float, block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                     chunk_tokens: int = 512, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     return_lse: bool = True, workspace: Optional[torch.Tensor] = None, stream=None
+                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Split-KV decode over a paged E4M3 KV cache (uint8 codes). q [B,Hq,D] bf16; k_cache [pages,Hkv,16,D];
+    v_cache_t [pages,Hkv,D,16] (each page transposed); cached values are code value * scale."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.uint8, 4)
+    _need(v_cache_t, "v_cache_t", torch.uint8, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    P, Hkv, page, D = k_cache.shape
+    if tuple(v_cache_t.shape) != (P, Hkv, D, page):
+        raise LcattnError(2, "v_cache_t must be [pages, Hkv, head_dim, page_size] for k_cache [pages, Hkv, page_size, "
+                             "head_dim]")
+    if block_table.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
+        raise LcattnError(2, "block_table and seq_lens need one row per sequence of q")
+    _same_device(q.device, (k_cache, "k_cache"), (v_cache_t, "v_cache_t"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens"))
+    shp = _decode_shape(q, k_cache, block_table, chunk_tokens, scale)
+    need = int(lib.attn_decode_workspace_bytes(ctypes.byref(shp), int(max_seq_len)))
+    ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _need(ws, "workspace", torch.uint8)
+    _same_device(q.device, (ws, "workspace"))
+    o = torch.empty_like(q) if out is None else out
+    _like(o, "out", q.shape, torch.bfloat16, q.device)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.attn_decode_paged_fp8(ctypes.byref(shp), _ptr(q), _ptr(k_cache), _ptr(v_cache_t), float(k_scale),
+                                     float(v_scale), _ptr(block_table), _ptr(seq_lens), int(max_seq_len), _ptr(o),
+                                     _ptr(lse), _ptr(ws), ws.numel(), _stream(stream, q.device)))
     return o, lse

@@ -219,10 +219,13 @@ size_t attn_decode_workspace_bytes(const attn_decode_shape_t* shape, int32_t max
                                           max_seq_len);
 }
 
-attn_status_t attn_decode_paged(const attn_decode_shape_t* shape, const void* q, const void* k_cache,
-                                const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                                int32_t max_seq_len, void* o, float* lse, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+namespace {
+
+// Checks and problem set-up shared by the bf16 and fp8 decode entry points.
+attn_status_t decode_problem(const attn_decode_shape_t* shape, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                             int32_t max_seq_len, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                             lcattn::DecodeProblem& p) {
     attn_status_t st = check_decode_shape(shape, max_seq_len);
     if (st != ATTN_OK) return st;
     if ((st = check_ptrs({q, block_table, seq_lens, o})) != ATTN_OK) return st;
@@ -236,7 +239,6 @@ attn_status_t attn_decode_paged(const attn_decode_shape_t* shape, const void* q,
         return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
-    lcattn::DecodeProblem p;
     p.q = q;
     p.k_cache = k_cache;
     p.v_cache = v_cache;
@@ -254,7 +256,34 @@ attn_status_t attn_decode_paged(const attn_decode_shape_t* shape, const void* q,
     p.chunk = shape->chunk_tokens;
     p.max_seq_len = max_seq_len;
     p.scale = shape->scale;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+attn_status_t attn_decode_paged(const attn_decode_shape_t* shape, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                                int32_t max_seq_len, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    lcattn::DecodeProblem p;
+    const attn_status_t st = decode_problem(shape, q, k_cache, v_cache, block_table, seq_lens, max_seq_len, o, lse,
+                                            workspace, workspace_bytes, p);
+    if (st != ATTN_OK) return st;
     return hip_status(lcattn::launch_decode_paged(p, workspace, static_cast<hipStream_t>(stream)), "attn_decode_paged");
+}
+
+attn_status_t attn_decode_paged_fp8(const attn_decode_shape_t* shape, const void* q, const uint8_t* k_cache,
+                                    const uint8_t* v_cache_t, float k_scale, float v_scale,
+                                    const int32_t* block_table, const int32_t* seq_lens, int32_t max_seq_len,
+                                    void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+        return fail(ATTN_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
+    lcattn::DecodeProblem p;
+    const attn_status_t st = decode_problem(shape, q, k_cache, v_cache_t, block_table, seq_lens, max_seq_len, o, lse,
+                                            workspace, workspace_bytes, p);
+    if (st != ATTN_OK) return st;
+    return hip_status(lcattn::launch_decode_paged_fp8(p, k_scale, v_scale, workspace, static_cast<hipStream_t>(stream)),
+                      "attn_decode_paged_fp8");
 }
 
 }  // extern "C"

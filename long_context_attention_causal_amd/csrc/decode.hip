@@ -345,6 +345,210 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const CombineArgs a
     if (a.lse && lane == 0) a.lse[bh] = M + logf(sw);
 }
 
+// ------------------------------------------------------------------------------------------------- fp8 cache
+// The same split over an E4M3 cache: K pages token-major [16 x D] bytes, V pages transposed [D x 16] bytes, one
+// scale per cache. A lane's MFMA operands come straight from HBM: 8 bytes of a key row for the S^T product and 4
+// consecutive tokens of one head-dim row of V^T for the O^T product, each widened to bf16 by the hardware
+// conversion (exact: every E4M3 value is a bf16 number), so no LDS is needed until the merge. k_scale is folded
+// into the exponent scale and v_scale into the final normalisation.
+struct SplitArgs8 {
+    const uint16_t* q;
+    const uint8_t* kc;
+    const uint8_t* vc;
+    const int32_t* bt;
+    const int32_t* lens;
+    float* opart;
+    float* lpart;
+    int B, Hq, Hkv, G, max_pages, num_pages, C, chunk, ppw;
+    float c2;       // softmax scale * log2(e) * k_scale
+    float vscale;
+};
+
+// bytes 0-1 (HI false) or 2-3 (HI true) of w as two bf16
+template <bool HI>
+__device__ __forceinline__ uint32_t widen2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+template <int D, int PB>
+struct Batch8 {
+    u32x2 k[PB][D / 32];     // 8 key bytes per 32-wide slice of the head dim
+    uint32_t v[PB][D / 16];  // 4 token bytes per 16-row tile of the head dim
+    int tok0;
+};
+
+template <int D, int NW, int PB>
+__global__ __launch_bounds__(NW * 64) void decode_split_fp8_kernel(const SplitArgs8 a) {
+    constexpr int KS = D / 32, DT = D / 16;
+    __shared__ float red_o[NW * 16 * D];
+    __shared__ float red_m[NW][16], red_l[NW][16];
+    const int g = (int)(blockIdx.x % a.Hkv), c = (int)(blockIdx.x / a.Hkv), b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, grp = lane >> 4;
+    const int L = a.lens[b];
+    const int wpage0 = c * (a.chunk / kPage) + w * a.ppw;
+    const int32_t* btrow = a.bt + (size_t)b * a.max_pages;
+    const int my_page = wpage0 + lane;
+    const int my_pid = (lane < a.ppw && my_page < a.max_pages) ? btrow[my_page] : 0;
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = n < a.G ? __builtin_bit_cast(bf16x8, load16(a.q + ((size_t)b * a.Hq + g * a.G + n) * D + 32 * ks +
+                                                                 8 * grp))
+                         : bf16x8{};
+    if (c * a.chunk >= L) return;  // uniform over the work-group
+
+    const int npages_seq = (L + kPage - 1) / kPage;
+    const int nbatch = ((a.ppw + 2 * PB - 1) / (2 * PB)) * 2;
+    constexpr int kLoads = (KS + DT) * PB;   // vector loads per batch
+    static_assert(kLoads < 64, "vmcnt holds at most 63");
+
+    auto issue = [&](int bi, Batch8<D, PB>& bt) {
+        bt.tok0 = (wpage0 + bi * PB) * kPage;
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+            const int lp = wpage0 + bi * PB + p;
+            const bool inrange = bi * PB + p < a.ppw && lp < npages_seq && lp < a.max_pages;
+            int pid = inrange ? __builtin_amdgcn_readlane(my_pid, min(bi * PB + p, 63)) : 0;
+            int valid = inrange ? min(kPage, L - lp * kPage) : 0;
+            if ((unsigned)pid >= (unsigned)a.num_pages) {
+                pid = 0;
+                valid = 0;
+            }
+            const uint8_t* kbase = a.kc + ((size_t)pid * a.Hkv + g) * (size_t)(kPage * D);
+            const uint8_t* vbase = a.vc + ((size_t)pid * a.Hkv + g) * (size_t)(kPage * D);
+            // key rows past the sequence end read as zeros; the value page is read whole (its tokens are the
+            // inner dimension) and its bytes past the end are cleared below
+            const __amdgpu_buffer_rsrc_t kr =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kbase), (short)0, valid * D, 0x00020000);
+            const __amdgpu_buffer_rsrc_t vr =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vbase), (short)0, valid ? kPage * D : 0,
+                                                  0x00020000);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                bt.k[p][ks] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                            kr, n * D + 32 * ks + 8 * grp, 0, 0));
+            const int nv = min(max(valid - 4 * grp, 0), 4);   // this lane's tokens 4*grp .. 4*grp+3 that exist
+            const uint32_t keep = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                bt.v[p][dt] = __builtin_amdgcn_raw_buffer_load_b32(vr, (16 * dt + n) * kPage + 4 * grp, 0, 0) & keep;
+        }
+    };
+
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{};
+    float m = -INFINITY, l = 0.0f;
+    bf16x2 ones;
+    ones[0] = (__bf16)1.0f;
+    ones[1] = (__bf16)1.0f;
+
+    auto run = [&](int bi, Batch8<D, PB>& cur, Batch8<D, PB>& nxt) {
+        issue(bi + 1, nxt);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (kLoads & 15) | ((kLoads >> 4) << 14));
+        f32x4 s[PB];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+            s[p] = f32x4{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 kw = {widen2<false>(cur.k[p][ks][0]), widen2<true>(cur.k[p][ks][0]),
+                                  widen2<false>(cur.k[p][ks][1]), widen2<true>(cur.k[p][ks][1])};
+                s[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qf[ks], s[p], 0, 0, 0);
+            }
+            const int tok = cur.tok0 + p * kPage + 4 * grp;
+            const bool page_in_wave = bi * PB + p < a.ppw;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (tok + r >= L || !page_in_wave) s[p][r] = -INFINITY;
+                mx = fmaxf(mx, s[p][r]);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mxs = mx * a.c2;
+        if (mxs > m) {
+            const float alpha = __builtin_amdgcn_exp2f(m - mxs);
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+            m = mxs;
+        }
+        const float bias = (m == -INFINITY) ? 0.0f : -m;
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[p][0], a.c2, bias));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[p][1], a.c2, bias));
+            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[p][2], a.c2, bias));
+            const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[p][3], a.c2, bias));
+            const uint32_t w0 = pack_bf16x2(p0, p1), w1 = pack_bf16x2(p2, p3);
+            const bf16x4 pb = __builtin_bit_cast(bf16x4, (u32x2{w0, w1}));
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, l, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, l, false);
+            // V^T[d = 16*dt + n][tokens 4*grp .. 4*grp+3] is the A operand of the 16x16x16 product as loaded
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const u32x2 vw = {widen2<false>(cur.v[p][dt]), widen2<true>(cur.v[p][dt])};
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vw), pb, o[dt], 0, 0, 0);
+            }
+        }
+    };
+
+    Batch8<D, PB> ba, bb;
+    issue(0, ba);
+    for (int bi = 0; bi < nbatch; bi += 2) {
+        run(bi, ba, bb);
+        run(bi + 1, bb, ba);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // the empty batch issued last
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (grp == 0) {
+        red_m[w][n] = m;
+        red_l[w][n] = l;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red_o[(w * 16 + n) * D + 16 * dt + 4 * grp + r] = o[dt][r];
+    __syncthreads();
+    for (int e = tid; e < a.G * (D / 4); e += NW * 64) {
+        const int hn = e / (D / 4), d = 4 * (e % (D / 4));
+        float M = red_m[0][hn];
+#pragma unroll
+        for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, red_m[ww][hn]);
+        f32x4 acc = f32x4{};
+        float lsum = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            const float mw = red_m[ww][hn];
+            const float sc = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+            acc += sc * *reinterpret_cast<const f32x4*>(&red_o[(ww * 16 + hn) * D + d]);
+            lsum += sc * red_l[ww][hn];
+        }
+        const size_t row = ((size_t)b * a.C + c) * a.Hq + g * a.G + hn;
+        *reinterpret_cast<f32x4*>(&a.opart[row * D + d]) = acc * (a.vscale / lsum);
+        if (d == 0) a.lpart[row] = (M + log2f(lsum)) * kLn2;
+    }
+}
+
+template <int D, int NW>
+void launch_split8(int pb, dim3 grid, const SplitArgs8& a, hipStream_t s) {
+    const dim3 block(NW * 64);
+    if (pb == 2) hipLaunchKernelGGL((decode_split_fp8_kernel<D, NW, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_split_fp8_kernel<D, NW, 4>), grid, block, 0, s, a);
+}
+
+template <int D>
+void launch_split8(int nw, int pb, dim3 grid, const SplitArgs8& a, hipStream_t s) {
+    if (nw == 1) launch_split8<D, 1>(pb, grid, a, s);
+    else if (nw == 2) launch_split8<D, 2>(pb, grid, a, s);
+    else launch_split8<D, 4>(pb, grid, a, s);
+}
+
 template <int D, int NW>
 void launch_split(int pb, dim3 grid, const SplitArgs& a, hipStream_t s) {
     const dim3 block(NW * 64);
@@ -366,6 +570,63 @@ size_t decode_workspace_bytes(int B, int Hq, int D, int chunk, int max_seq_len) 
     const size_t o_bytes = (size_t)B * Hq * (C ? C : 1) * D * sizeof(float);
     const size_t l_bytes = (size_t)B * Hq * (C ? C : 1) * sizeof(float);
     return ((o_bytes + 255) / 256) * 256 + ((l_bytes + 255) / 256) * 256;
+}
+
+// The chunk merge both caches share.
+hipError_t launch_combine(const DecodeProblem& p, const float* opart, const float* lpart, int C, hipStream_t s) {
+    CombineArgs cb;
+    cb.opart = opart;
+    cb.lpart = lpart;
+    cb.lens = p.seq_lens;
+    cb.o = static_cast<uint16_t*>(p.o);
+    cb.lse = p.lse;
+    cb.B = p.B;
+    cb.Hq = p.Hq;
+    cb.C = C;
+    cb.chunk = p.chunk;
+    const dim3 grid2((unsigned)((p.B * p.Hq + 3) / 4));
+    if (p.D == 64) hipLaunchKernelGGL((decode_combine_kernel<64>), grid2, dim3(256), 0, s, cb);
+    else hipLaunchKernelGGL((decode_combine_kernel<128>), grid2, dim3(256), 0, s, cb);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_paged_fp8(const DecodeProblem& p, float k_scale, float v_scale, void* workspace,
+                                   hipStream_t s) {
+    const int C = (p.max_seq_len + p.chunk - 1) / p.chunk;
+    const size_t o_bytes = (size_t)p.B * p.Hq * (C ? C : 1) * p.D * sizeof(float);
+    SplitArgs8 a;
+    a.q = static_cast<const uint16_t*>(p.q);
+    a.kc = static_cast<const uint8_t*>(p.k_cache);
+    a.vc = static_cast<const uint8_t*>(p.v_cache);
+    a.bt = p.block_table;
+    a.lens = p.seq_lens;
+    a.opart = static_cast<float*>(workspace);
+    a.lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((o_bytes + 255) / 256) * 256);
+    a.B = p.B;
+    a.Hq = p.Hq;
+    a.Hkv = p.Hkv;
+    a.G = p.Hq / p.Hkv;
+    a.max_pages = p.max_pages;
+    a.num_pages = p.num_pages;
+    a.C = C ? C : 1;
+    a.chunk = p.chunk;
+    // one wave per work-group while a wave's pages fit its 64 block-table lanes: with half the bytes per page a
+    // wave streams its whole share of the chunk (one wave of 32 pages measured 4% faster than two of 16 on the
+    // paged workload; 8 pages per batch was slower than 4)
+    const int pages = p.chunk / kPage;
+    const int nw = pages <= 64 ? 1 : pages <= 128 ? 2 : 4;
+    const int pb = p.D == 64 ? 4 : 2;
+    a.ppw = p.chunk / kPage / nw;
+    a.c2 = p.scale * kLog2e * k_scale;
+    a.vscale = v_scale;
+    if (C > 0) {
+        const dim3 grid((unsigned)(C * p.Hkv), (unsigned)p.B);
+        if (p.D == 64) launch_split8<64>(nw, pb, grid, a, s);
+        else launch_split8<128>(nw, pb, grid, a, s);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_combine(p, a.opart, a.lpart, a.C, s);
 }
 
 hipError_t launch_decode_paged(const DecodeProblem& p, void* workspace, hipStream_t s) {
@@ -402,20 +663,7 @@ hipError_t launch_decode_paged(const DecodeProblem& p, void* workspace, hipStrea
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    CombineArgs cb;
-    cb.opart = a.opart;
-    cb.lpart = a.lpart;
-    cb.lens = p.seq_lens;
-    cb.o = static_cast<uint16_t*>(p.o);
-    cb.lse = p.lse;
-    cb.B = p.B;
-    cb.Hq = p.Hq;
-    cb.C = a.C;
-    cb.chunk = p.chunk;
-    const dim3 grid2((unsigned)((p.B * p.Hq + 3) / 4));
-    if (p.D == 64) hipLaunchKernelGGL((decode_combine_kernel<64>), grid2, dim3(256), 0, s, cb);
-    else hipLaunchKernelGGL((decode_combine_kernel<128>), grid2, dim3(256), 0, s, cb);
-    return hipGetLastError();
+    return launch_combine(p, a.opart, a.lpart, a.C, s);
 }
 
 }  // namespace lcattn

@@ -65,5 +65,8 @@ struct DecodeProblem {
 
 size_t decode_workspace_bytes(int B, int Hq, int D, int chunk, int max_seq_len);
 hipError_t launch_decode_paged(const DecodeProblem& p, void* workspace, hipStream_t s);
+// k_cache holds E4M3 codes [pages, Hkv, 16, D], v_cache E4M3 codes transposed per page [pages, Hkv, D, 16]
+hipError_t launch_decode_paged_fp8(const DecodeProblem& p, float k_scale, float v_scale, void* workspace,
+                                   hipStream_t s);
 
 }  // namespace lcattn

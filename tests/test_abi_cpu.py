@@ -31,14 +31,14 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     decl = declared_functions()
-    assert len(decl) == 9
+    assert len(decl) == 10
     for name in decl:
         assert hasattr(L, name), name
     assert set(decl) == set(lca.EXPORTS)
 
 
 def test_version_and_status_strings(L):
-    assert lca.abi_version() == 2
+    assert lca.abi_version() == 3
     for st in range(7):
         assert L.attn_status_string(st)
     assert L.attn_status_string(99) == b"unknown status"
@@ -154,6 +154,34 @@ def dshape(B=4, Hq=16, Hkv=2, D=64, page=16, maxp=64, pages=100, chunk=512, scal
 def test_decode_rejects(L, s, maxlen, code):
     assert L.attn_decode_paged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, maxlen, FAKE, None, FAKE, 1 << 40,
                                None) == code
+
+
+def decode8(L, s, maxlen, ks=1.0, vs=1.0, ws=1 << 40, k=FAKE, bt=FAKE, wsp=FAKE):
+    return L.attn_decode_paged_fp8(ctypes.byref(s), FAKE, k, FAKE, ks, vs, bt, FAKE, maxlen, FAKE, None, wsp, ws, None)
+
+
+@pytest.mark.parametrize("s,maxlen,ks,vs,code", [
+    (dshape(), 100, 0.0, 1.0, 2),
+    (dshape(), 100, 1.0, -1.0, 2),
+    (dshape(), 100, math.nan, 1.0, 2),
+    (dshape(), 100, 1.0, math.inf, 2),
+    (dshape(Hq=15), 100, 1.0, 1.0, 2),
+    (dshape(D=80), 100, 1.0, 1.0, 3),
+    (dshape(page=32), 100, 1.0, 1.0, 3),
+    (dshape(), 64 * 16 + 1, 1.0, 1.0, 2),
+])
+def test_decode_fp8_rejects(L, s, maxlen, ks, vs, code):
+    assert decode8(L, s, maxlen, ks, vs) == code
+    assert L.attn_last_error()
+
+
+def test_decode_fp8_checks_like_bf16(L):
+    s = dshape()
+    need = L.attn_decode_workspace_bytes(ctypes.byref(s), 1000)
+    assert decode8(L, s, 1000, ws=need - 1) == 5
+    assert decode8(L, s, 1000, ws=need, wsp=FAKE + 64) == 4
+    assert decode8(L, s, 1000, ws=need, bt=None) == 1
+    assert decode8(L, s, 1000, ws=need, k=None) == 1
 
 
 def test_decode_workspace(L):

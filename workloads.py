@@ -52,19 +52,23 @@ def f64_from_bf16_bits(u: np.ndarray) -> np.ndarray:
 
 def e4m3_codes_from_f32(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to 8-bit E4M3 codes (OCP OFP8: bias 7, 3 mantissa bits, subnormals below 2^-6, largest
-    finite 448) with round-to-nearest-even, saturating at +-448; returns uint8 codes. Inputs are assumed finite."""
-    x = np.asarray(x, dtype=np.float32).astype(np.float64)
-    a = np.minimum(np.abs(x), 448.0)
-    _, ex = np.frexp(a)                       # a = f * 2^ex with f in [0.5, 1): binade exponent ex - 1
-    e = np.maximum(ex.astype(np.int64) - 1, -6)
-    quantum = np.exp2((e - 3).astype(np.float64))
-    m = np.round(a / quantum).astype(np.int64)   # numpy rounds halves to even; a / quantum is exact
-    carry = m == 16
-    e = np.where(carry, e + 1, e)
-    m = np.where(carry, 8, m)
-    sub = m < 8                               # only where e == -6: the subnormal range
-    code = np.where(sub, m, ((e + 7) << 3) | (m - 8))
-    code = np.where(x < 0, code | 0x80, code)
+    finite 448) with round-to-nearest-even, saturating at +-448; returns uint8 codes. Inputs are assumed finite.
+
+    Normal range: the fp32 pattern is rounded to its top 3 mantissa bits in integer arithmetic (a carry moves into
+    the exponent) and the exponent is rebased from 127 to 7. Below 2^-6 the code is the magnitude in units of
+    2^-9, rounded half to even."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x), np.float32(448.0))
+    u = a.view(np.uint32)
+    code = (u >> np.uint32(20)) & np.uint32(1)
+    code += u
+    code += np.uint32(0x7FFFF)
+    code >>= np.uint32(20)
+    code -= np.uint32(120 << 3)                                  # wraps below 2^-6; replaced next
+    small = a < np.float32(2.0 ** -6)
+    if small.any():
+        code[small] = np.rint(a[small] * np.float32(512.0)).astype(np.uint32)   # exact scaling, ties to even
+    code |= (x.view(np.uint32) >> np.uint32(24)) & np.uint32(0x80)   # the sign bit
     return code.astype(np.uint8)
 
 
