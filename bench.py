@@ -64,6 +64,9 @@ def main():
     ap.add_argument("--long-reps", type=int, default=3)
     ap.add_argument("--only", choices=["dense", "dense32k", "sparse", "decode", "decode8", "copy"], default=None,
                     help="run one path alone (for profiler runs); prints a short JSON line with its mean time")
+    ap.add_argument("--selector-sweep", action="store_true",
+                    help="selector footprint and block-size sweep (N 32K..256K, blocks 64/128/256, both rescue "
+                         "modes); prints one JSON document instead of the bench line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (each GPU would run an "
@@ -85,6 +88,9 @@ def main():
 
     if args.only:
         run_only(args, lca, W, torch, np, to_dev, dev)
+        return
+    if args.selector_sweep:
+        selector_sweep(lca, W, torch, np, to_dev, dev)
         return
 
     # ---------------------------------------------------------------------------------------- inputs
@@ -385,6 +391,76 @@ def main():
         "paths": paths,
     }
     print(json.dumps(line), flush=True)
+
+
+def selector_sweep(lca, W, torch, np, to_dev, dev):
+    """Selector footprint and block-size sweep on the planted workload shape (B1 Hq32 Hkv4 D128): for N of 32K,
+    64K, 128K and 256K and blocks of 64, 128 and 256 keys (up to 4096 blocks), in both rescue modes, the mask
+    build's workspace and output bytes, its measured peak device memory beyond the inputs, its time, the mask
+    density, the planted blocks kept in their query's row, and the sparse pass's time over the mask. The centroid
+    budget is 10% at 32K and 5% above, rescue alpha 1. Q/K/V are drawn once per N; the outliers are planted
+    afresh for each block size."""
+    Hq, Hkv, D = 32, 4, 128
+    scale = 1.0 / math.sqrt(D)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    rows = []
+    for N in (32768, 65536, 131072, 262144):
+        seed = 100 + N // 32768
+        keep = 100 if N <= 32768 else 50
+        log(f"selector sweep: generating N={N}")
+        base = W.dense_inputs(seed, 1, Hq, Hkv, N, D, "bf16")
+        k_clean = base.k.copy()
+        q, v = to_dev(base.q), to_dev(base.v)
+        o = torch.empty_like(q)
+        for block in (64, 128, 256):
+            nb = N // block
+            if nb > 4096:
+                continue
+            base.k[...] = k_clean
+            W.plant_outliers(base, seed, block)
+            k = to_dev(base.k)
+            for mode in (0, 1):
+                log(f"selector sweep: N={N} block={block} rescue_mode={mode}")
+                ws = lca.block_mask_workspace_bytes(q, k, block, keep, 1.0, scale=scale, rescue_mode=mode)
+                out_bytes = Hq * nb * nb * (1 + 4) + Hq * nb * 4
+                torch.cuda.synchronize()
+                torch.cuda.empty_cache()
+                torch.cuda.reset_peak_memory_stats()
+                before = torch.cuda.memory_allocated()
+                m = lca.block_mask_build(q, k, block, keep, 1.0, scale=scale, want_radius_stats=False,
+                                         rescue_mode=mode)
+                torch.cuda.synchronize()
+                peak = torch.cuda.max_memory_allocated() - before
+                t_mask = timed(lambda: lca.block_mask_build(q, k, block, keep, 1.0, scale=scale, outputs=m,
+                                                            rescue_mode=mode), 5)
+                t_sparse = timed(lambda: lca.prefill_block_sparse(q, k, v, m.kv_count, m.kv_index, block,
+                                                                  scale=scale, out=o, return_lse=False), 3)
+                cnt = m.kv_count.cpu().numpy().astype(np.int64)
+                idx = torch.tensor([[b, h, t // block, j] for (b, g, j, u, h, t) in base.planted], device=dev).T
+                kept = int(m.mask[idx[0], idx[1], idx[2], idx[3]].sum().item())
+                rows.append({"N": N, "block": block, "rescue_mode": mode, "keep_permille": keep,
+                             "workspace_bytes": ws, "output_bytes": out_bytes, "peak_bytes_measured": int(peak),
+                             "mask_ms": t_mask, "sparse_ms": t_sparse,
+                             "density": float(cnt.sum() / (Hq * nb * (nb + 1) / 2)),
+                             "planted_kept": kept, "planted": len(base.planted)})
+                print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+                del m
+            del k
+        del q, v, o, base, k_clean
+        torch.cuda.empty_cache()
+    print(json.dumps({"selector_sweep": rows}), flush=True)
 
 
 def run_only(args, lca, W, torch, np, to_dev, dev):

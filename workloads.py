@@ -135,17 +135,29 @@ def dense_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, D: int, dtype: st
 
 def planted_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, D: int, block: int,
                    planted_per_mille: int = 50) -> PrefillInputs:
-    """Dense bf16 inputs plus planted high-attention keys.
+    """Dense bf16 inputs plus planted high-attention keys (plant_outliers)."""
+    if N % block:
+        raise ValueError("N must be a multiple of block")
+    inp = dense_inputs(seed, B, Hq, Hkv, N, D, "bf16")
+    plant_outliers(inp, seed, block, planted_per_mille)
+    return inp
+
+
+def plant_outliers(inp: PrefillInputs, seed: int, block: int, planted_per_mille: int = 50) -> PrefillInputs:
+    """Overwrite keys of bf16 inputs in place with planted high-attention keys, for blocks of `block` rows.
 
     Per (batch, kv-head g): choose nKB*planted_per_mille//1000 key blocks j without replacement from
     [0, nKB-2]. For each: a slot u in [0, block), a later query block i in [j+1, nQB-1], a query row t in block i
     and a query head h of g's group are drawn, and key row j*block+u of kv-head g is overwritten with
     bf16(6.0 * q[b, h, t]). The key then scores far above its neighbours for that query while the block's mean
-    barely moves, which is the geometry the mean-dilution section describes."""
+    barely moves, which is the geometry the mean-dilution section describes. The draws come from the seed's own
+    "planted" stream, so the same seed and block give the same plants whatever was drawn before."""
+    B, Hq, N, D = inp.q.shape
+    Hkv = inp.k.shape[1]
     if N % block:
         raise ValueError("N must be a multiple of block")
-    inp = dense_inputs(seed, B, Hq, Hkv, N, D, "bf16")
     inp.block = block
+    inp.planted = []
     rng = streams(seed, ["q", "k", "v", "planted", "rows"])["planted"]
     nb = N // block
     G = Hq // Hkv
