@@ -302,6 +302,32 @@ def decode_inputs_fp8(seed: int, B: int, Hq: int, Hkv: int, D: int, page: int, l
                            block_table=bt, seq_lens=lens, page=page, scale=float(1.0 / np.sqrt(D)))
 
 
+@dataclass
+class PagedPrefillInputs:
+    """A chunk of Nq new tokens per sequence over a paged bf16 cache that already holds them: q [B,Hq,Nq,D]
+    (bf16 bits), the cache, block table and lengths of DecodeInputs (seq_lens[b] >= Nq), and a sliding window
+    (0 = none)."""
+    q: np.ndarray
+    cache: DecodeInputs
+    window: int
+
+    @property
+    def scale(self) -> float:
+        return self.cache.scale
+
+
+def paged_prefill_inputs(seed: int, B: int, Hq: int, Hkv: int, D: int, Nq: int, page: int, len_lo: int,
+                         len_hi: int, window: int = 0, seq_lens: Optional[np.ndarray] = None) -> PagedPrefillInputs:
+    """The paged cache of decode_inputs (lengths uniform on [len_lo, len_hi], len_lo >= Nq, NaN past each end)
+    plus Nq query rows per sequence and head from a stream of their own."""
+    if len_lo < Nq and seq_lens is None:
+        raise ValueError("every sequence must hold the chunk: len_lo >= Nq")
+    cache = decode_inputs(seed, B, Hq, Hkv, D, page, len_lo, len_hi, seq_lens=seq_lens)
+    rq = streams(seed, ["q", "k", "v", "lens", "perm", "rows", "chunk_q"])["chunk_q"]
+    q = _normal_bf16(rq, (B, Hq, Nq, D))
+    return PagedPrefillInputs(q=q, cache=cache, window=int(window))
+
+
 # --------------------------------------------------------------------------------------------------------------
 # sampled query rows for large configurations
 # --------------------------------------------------------------------------------------------------------------
@@ -357,6 +383,13 @@ WORKLOADS = {
                                  keep_permille=50, alpha=1.0, q_lo_pct=50, q_hi_pct=90),
     "c5_decode_paged_bf16": dict(kind="decode", seed=5, B=32, Hq=64, Hkv=8, D=64, page=16, len_lo=1024,
                                  len_hi=32768, chunk=512),
+    # chunked prefill: the last 4096 tokens of a 32768-token sequence in a paged cache, the model shape above
+    "c6_paged_prefill_chunk": dict(kind="paged_prefill", seed=6, B=1, Hq=32, Hkv=4, D=128, Nq=4096, page=16,
+                                   len_lo=32768, len_hi=32768, window=0),
+    # sliding-window chunked prefill, the grouped-query, windowed layer shape (64 query heads, 8 kv heads,
+    # head_dim 64, window 128) over 8 sequences of 8K-16K tokens, 2048 new tokens each
+    "c7_paged_prefill_window": dict(kind="paged_prefill", seed=7, B=8, Hq=64, Hkv=8, D=64, Nq=2048, page=16,
+                                    len_lo=8192, len_hi=16384, window=128),
     # the same decode workload over an E4M3 KV cache (per-tensor scales 2^-6)
     "c5_decode_paged_fp8": dict(kind="decode_fp8", seed=5, B=32, Hq=64, Hkv=8, D=64, page=16, len_lo=1024,
                                 len_hi=32768, chunk=512, k_scale=2.0 ** -6, v_scale=2.0 ** -6),
@@ -372,6 +405,9 @@ def make(name: str):
         return planted_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["block"])
     if w["kind"] == "decode":
         return decode_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["D"], w["page"], w["len_lo"], w["len_hi"])
+    if w["kind"] == "paged_prefill":
+        return paged_prefill_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["D"], w["Nq"], w["page"], w["len_lo"],
+                                    w["len_hi"], w["window"])
     if w["kind"] == "decode_fp8":
         return decode_inputs_fp8(w["seed"], w["B"], w["Hq"], w["Hkv"], w["D"], w["page"], w["len_lo"], w["len_hi"],
                                  w["k_scale"], w["v_scale"])
