@@ -7,8 +7,9 @@ A step runs every variant once, each on its own synthetic workload, with inputs 
   sparse  block-mask build + block-sparse prefill, N32768 block 64, centroid budget 10%, rescue alpha 1
   decode  split-KV paged decode, B32 Hq64 Hkv8 D64, lengths U[1024, 32768], page 16, 512-token chunks
 `value` is the dense prefill's TFLOP/s (causal count 2*B*Hq*N^2*D over the kernel's own event-timed duration).
-After the timed steps the decode workload is also run over an fp8 (E4M3) copy of its cache, and the long-context
-lines are measured on their own: dense prefill at 32K and 128K and the
+After the timed steps the decode workload is also run over an fp8 (E4M3) copy of its cache, chunked prefill over a
+paged cache is timed (a 4K chunk closing a 32K sequence; a 128-token-window chunk over 8 sequences), and the
+long-context lines are measured on their own: dense prefill at 32K and 128K and the
 128K mask + sparse pass (speedup over this build's dense kernel at the same length), and at 32K and 128K the mask
 built with the query-aware rescue (rescue_mode 1) and the sparse pass over it. The fp64 CPU oracle is timed
 on the host (cpu_baseline) on the headline workload. One JSON line goes to stdout.
@@ -264,7 +265,9 @@ def main():
         "cold_ms": float(np.mean(cold8_ms)), "cold_ms_median": float(np.median(cold8_ms)),
         "cold_gbs": dec8_bytes / (float(np.mean(cold8_ms)) * 1e-3) / 1e9,
         "cold_pct_hbm_peak": 100 * dec8_bytes / (float(np.mean(cold8_ms)) * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "speedup_vs_bf16_cold": float(np.mean(cold_ms)) / float(np.mean(cold8_ms))}
+        "speedup_vs_bf16_cold": float(np.mean(cold_ms)) / float(np.mean(cold8_ms)),
+        "measured_hbm_bytes": (lambda a, b: None if a is None or b is None else a + b)(
+            measured_traffic("decode_split_fp8_c5", "decode.hip"), measured_traffic("decode_combine_fp8_c5", "decode.hip"))}
 
     def time_calls(fn, reps):
         fn()
@@ -305,6 +308,29 @@ def main():
                 "speedup_vs_dense_kernel_only": t_dense_same_n / ts,
                 "speedup_vs_dense_incl_mask": t_dense_same_n / (ts + tm),
                 "planted_kept": planted_kept(m.mask, planted, blk)}
+
+    # chunked prefill over a paged cache: a 4K chunk closing a 32K sequence, and a windowed chunk over 8 sequences
+    def paged_line(name, reps):
+        w = W.WORKLOADS[name]
+        log(f"generating {name}")
+        p = W.make(name)
+        c = p.cache
+        qp, kp, vp = to_dev(p.q), to_dev(c.k_cache), to_dev(c.v_cache)
+        btp, slp = torch.from_numpy(c.block_table).to(dev), torch.from_numpy(c.seq_lens).to(dev)
+        op = torch.empty_like(qp)
+        log(f"paged prefill {name}")
+        t, sp = time_calls(lambda: lca.prefill_paged(qp, kp, vp, btp, slp, window=w["window"], scale=p.scale, out=op,
+                                                     return_lse=False), reps)
+        Lp = c.seq_lens.astype(np.int64)
+        Nq = w["Nq"]
+        pos = (Lp[:, None] - Nq) + np.arange(Nq)[None, :]
+        keys = np.minimum(pos + 1, w["window"]) if w["window"] > 0 else pos + 1
+        fl = 4.0 * w["D"] * w["Hq"] * float(keys.sum())
+        return {"ms": t, **sp, "tflops": fl / (t * 1e-3) / 1e12, "pct_bf16_peak": 100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "new_tokens_per_s": w["B"] * Nq / (t * 1e-3), "flop": fl}
+
+    paths["paged_prefill_c6_chunk4k_of_32k"] = paged_line("c6_paged_prefill_chunk", 20)
+    paths["paged_prefill_c7_window128"] = paged_line("c7_paged_prefill_window", 20)
 
     if not args.no_long:
         log("dense prefill at 32K")

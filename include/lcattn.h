@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define LCATTN_ABI_VERSION 3
+#define LCATTN_ABI_VERSION 4
 
 typedef enum {
     ATTN_OK = 0,
@@ -134,6 +134,33 @@ attn_status_t attn_block_mask_build(const attn_shape_t* shape, const attn_mask_p
 attn_status_t attn_prefill_block_sparse(const attn_shape_t* shape, int32_t block_size, const void* q,
                                         const void* k, const void* v, const int32_t* kv_count,
                                         const int32_t* kv_index, void* o, float* lse, void* stream);
+
+/* Chunked prefill over a paged cache: q [batch, heads_q, q_len, head_dim]; caches as for decode. */
+typedef struct {
+    int32_t batch, heads_q, heads_kv, head_dim, q_len, page_size, max_pages_per_seq, num_pages;
+    int32_t window;  /* 0: causal over the whole sequence; > 0: each query sees its `window` latest keys */
+    float scale;
+} attn_paged_prefill_shape_t;
+
+/*
+ * Chunked prefill over a paged KV cache, optionally with a sliding window ("attention-kernel-optimization",
+ * section "PagedAttention": fixed-size pages found through a block table; "Your Context Length Decides What a
+ * Kernel Is Worth": sliding-window attention on some layers). Sequence b holds seq_lens[b] = L_b tokens in its
+ * pages, the last q_len of which are the new chunk (their K/V already written); chunk row r sits at position
+ * p = L_b - q_len + r and sees the keys t <= p, and with window > 0 only those with t > p - window. Each row is
+ * exact attention over those keys with the dense prefill's arithmetic.
+ *   q            bf16 [batch, heads_q, q_len, head_dim]
+ *   k_cache, v_cache  bf16 [num_pages, heads_kv, page_size, head_dim]; at most 2^32 - 1 bytes each
+ *   block_table  int32 [batch, max_pages_per_seq]; entries below ceil(L_b / page_size) are read (trusted, in
+ *                [0, num_pages); an entry outside reads as zeros)
+ *   seq_lens     int32 [batch], each in [q_len, max_pages_per_seq * page_size] (trusted)
+ *   o            bf16 like q; lse optional fp32 [batch, heads_q, q_len] (NULL to skip).
+ * Cache slots at or past a sequence's end may hold any bits; they never reach the output. q_len 0 is a no-op.
+ * Supported: head_dim 64 or 128, page_size 16.
+ */
+attn_status_t attn_prefill_paged(const attn_paged_prefill_shape_t* shape, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table, const int32_t* seq_lens, void* o,
+                                 float* lse, void* stream);
 
 /* Bytes of device workspace attn_decode_paged needs when no sequence is longer than max_seq_len. */
 size_t attn_decode_workspace_bytes(const attn_decode_shape_t* shape, int32_t max_seq_len);

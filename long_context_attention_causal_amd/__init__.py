@@ -46,6 +46,13 @@ class AttnMaskParams(ctypes.Structure):
                 ("rescue_mode", ctypes.c_int32)]
 
 
+class AttnPagedPrefillShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("q_len", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
 class AttnDecodeShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
@@ -54,8 +61,8 @@ class AttnDecodeShape(ctypes.Structure):
 
 
 EXPORTS = ("attn_prefill_dense", "attn_block_mask_workspace_bytes", "attn_block_mask_build",
-           "attn_prefill_block_sparse", "attn_decode_workspace_bytes", "attn_decode_paged", "attn_decode_paged_fp8",
-           "attn_status_string", "attn_last_error", "attn_abi_version")
+           "attn_prefill_block_sparse", "attn_prefill_paged", "attn_decode_workspace_bytes", "attn_decode_paged",
+           "attn_decode_paged_fp8", "attn_status_string", "attn_last_error", "attn_abi_version")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -91,6 +98,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                           vp, vp, vp, sz, vp]
     lib.attn_prefill_block_sparse.restype = i32
     lib.attn_prefill_block_sparse.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_prefill_paged.restype = i32
+    lib.attn_prefill_paged.argtypes = [ctypes.POINTER(AttnPagedPrefillShape), vp, vp, vp, vp, vp, vp, vp, vp]
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(AttnDecodeShape), i32]
     lib.attn_decode_paged.restype = i32
@@ -336,4 +345,36 @@ def decode_paged_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache_t: torch.Te
     _check(lib.attn_decode_paged_fp8(ctypes.byref(shp), _ptr(q), _ptr(k_cache), _ptr(v_cache_t), float(k_scale),
                                      float(v_scale), _ptr(block_table), _ptr(seq_lens), int(max_seq_len), _ptr(o),
                                      _ptr(lse), _ptr(ws), ws.numel(), _stream(stream, q.device)))
+    return o, lse
+
+
+def prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                  seq_lens: torch.Tensor, window: int = 0, scale: Optional[float] = None,
+                  out: Optional[torch.Tensor] = None, return_lse: bool = True, stream=None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill over a paged bf16 cache. q [B,Hq,Nq,D]: the last Nq of each sequence's seq_lens[b] tokens
+    (already in the cache [pages,Hkv,16,D]); window 0 = causal over the whole sequence, W > 0 = the W latest keys."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if k_cache.shape != v_cache.shape:
+        raise LcattnError(2, "k_cache and v_cache shapes differ")
+    B, Hq, Nq, D = q.shape
+    P, Hkv, page, D2 = k_cache.shape
+    if D2 != D:
+        raise LcattnError(2, "head_dim of q and cache differ")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise LcattnError(2, "block_table and seq_lens need one row per sequence of q")
+    _same_device(q.device, (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens"))
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    shp = AttnPagedPrefillShape(B, Hq, Hkv, D, Nq, page, block_table.shape[1], P, int(window), sc)
+    o = torch.empty_like(q) if out is None else out
+    _like(o, "out", q.shape, torch.bfloat16, q.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.attn_prefill_paged(ctypes.byref(shp), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                  _ptr(seq_lens), _ptr(o), _ptr(lse), _stream(stream, q.device)))
     return o, lse

@@ -272,6 +272,52 @@ attn_status_t attn_decode_paged(const attn_decode_shape_t* shape, const void* q,
     return hip_status(lcattn::launch_decode_paged(p, workspace, static_cast<hipStream_t>(stream)), "attn_decode_paged");
 }
 
+attn_status_t attn_prefill_paged(const attn_paged_prefill_shape_t* shape, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table, const int32_t* seq_lens, void* o,
+                                 float* lse, void* stream) {
+    if (!shape) return fail(ATTN_ERR_NULL, "shape is NULL");
+    const attn_paged_prefill_shape_t& s = *shape;
+    if (s.batch < 1 || s.heads_q < 1 || s.heads_kv < 1 || s.q_len < 0 || s.num_pages < 0 || s.max_pages_per_seq < 1 ||
+        s.window < 0)
+        return fail(ATTN_ERR_SHAPE, "batch, heads, max_pages_per_seq must be >= 1; q_len, num_pages, window >= 0");
+    if (s.heads_q % s.heads_kv) return fail(ATTN_ERR_SHAPE, "heads_q must be a multiple of heads_kv");
+    if (s.head_dim != 64 && s.head_dim != 128) return fail(ATTN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (s.page_size != 16) return fail(ATTN_ERR_UNSUPPORTED, "page_size must be 16");
+    if (!(std::isfinite(s.scale) && s.scale > 0.0f)) return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
+    if ((long long)s.q_len > (long long)s.max_pages_per_seq * s.page_size)
+        return fail(ATTN_ERR_SHAPE, "q_len exceeds max_pages_per_seq * page_size");
+    const unsigned long long cache_bytes =
+        (unsigned long long)s.num_pages * s.heads_kv * s.page_size * s.head_dim * 2ull;
+    if (cache_bytes > 0xFFFFFFFFull) return fail(ATTN_ERR_UNSUPPORTED, "a cache above 2^32 - 1 bytes");
+    // work-groups: ceil(q_len / positions per group) x batch x kv heads x head groups <= (q_len / 32 + 1) x batch x heads_q
+    if (((long long)s.q_len / 32 + 1) * s.batch * s.heads_q > 0x7FFFFFFFLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
+    if (s.q_len == 0) return ok();
+    if (s.num_pages == 0) return fail(ATTN_ERR_SHAPE, "q_len > 0 needs at least one cache page");
+    attn_status_t st = check_ptrs({q, k_cache, v_cache, block_table, seq_lens, o});
+    if (st != ATTN_OK) return st;
+    if (lse && !aligned16(lse)) return fail(ATTN_ERR_ALIGN, "lse must be 16-byte aligned");
+    lcattn::PagedPrefillProblem p;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_table = block_table;
+    p.seq_lens = seq_lens;
+    p.o = o;
+    p.lse = lse;
+    p.B = s.batch;
+    p.Hq = s.heads_q;
+    p.Hkv = s.heads_kv;
+    p.D = s.head_dim;
+    p.Nq = s.q_len;
+    p.max_pages = s.max_pages_per_seq;
+    p.num_pages = s.num_pages;
+    p.window = s.window;
+    p.cache_bytes = (size_t)cache_bytes;
+    p.scale = s.scale;
+    return hip_status(lcattn::launch_prefill_paged(p, static_cast<hipStream_t>(stream)), "attn_prefill_paged");
+}
+
 attn_status_t attn_decode_paged_fp8(const attn_decode_shape_t* shape, const void* q, const uint8_t* k_cache,
                                     const uint8_t* v_cache_t, float k_scale, float v_scale,
                                     const int32_t* block_table, const int32_t* seq_lens, int32_t max_seq_len,

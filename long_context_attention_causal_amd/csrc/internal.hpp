@@ -63,6 +63,21 @@ struct DecodeProblem {
     float scale;
 };
 
+// Chunked prefill over a paged bf16 cache ([num_pages, Hkv, 16, D]); q/o [B, Hq, Nq, D].
+struct PagedPrefillProblem {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    void* o;
+    float* lse;  // may be null
+    int B, Hq, Hkv, D, Nq, max_pages, num_pages, window;
+    size_t cache_bytes;   // bytes of one cache, below 2^32
+    float scale;
+};
+hipError_t launch_prefill_paged(const PagedPrefillProblem& p, hipStream_t s);
+
 size_t decode_workspace_bytes(int B, int Hq, int D, int chunk, int max_seq_len);
 hipError_t launch_decode_paged(const DecodeProblem& p, void* workspace, hipStream_t s);
 // k_cache holds E4M3 codes [pages, Hkv, 16, D], v_cache E4M3 codes transposed per page [pages, Hkv, D, 16]

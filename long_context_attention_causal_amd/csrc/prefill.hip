@@ -32,6 +32,7 @@ namespace lcattn {
 namespace {
 
 constexpr int kBN = 64;        // keys per KV tile
+constexpr int kPageTokens = 16; // tokens per page of a paged cache
 constexpr int kDenseWaves = 4; // waves per dense work-group
 constexpr float kSlack = 8.0f; // lazy-rescale threshold, log2 units
 
@@ -502,6 +503,156 @@ void prefill_dense_kernel(const DenseArgs a) {
     finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
 }
 
+// ---------------------------------------------------------------------------------------- paged prefill
+// Chunked prefill over a paged cache ("attention-kernel-optimization", section "PagedAttention"; sliding windows as
+// in "Your Context Length Decides What a Kernel Is Worth"): the dense kernel's work-groups, tile body and
+// single-buffered walk, with K/V tiles gathered from pages and an optional lower (window) bound on the keys.
+struct PagedArgs {
+    const uint16_t* q;
+    const uint16_t* kc;
+    const uint16_t* vc;
+    uint16_t* o;
+    float* lse;
+    const int32_t* bt;
+    const int32_t* lens;
+    int B, Hq, Hkv, Nq, G, max_pages, num_pages, window;
+    int HPW, NHG, PPW, n_ptiles;
+    uint32_t cache_bytes;   // bytes of one cache: the buffer view's size
+    float c2;
+};
+
+// Gathering tile loader: a 64-key tile spans four 16-token pages, and each 16-byte LDS slot's source row is read
+// from its page (one slab of 16 x D per page and kv head). Slots of keys at or past the sequence end, or on a page
+// the table does not give, point past the view and read zeros.
+// The slot's row and source offset are recomputed per load (a few integer operations) rather than kept, which
+// holds the kernel inside three waves' register budget.
+template <int D, int NW, int STR>
+struct PagedLoader {
+    static constexpr int LOADS = kBN * STR / 1024;
+    static constexpr int PER = (LOADS + NW - 1) / NW;
+    static constexpr int SPR = STR / 16;
+    int first;   // this wave's first load slot
+    int lane;
+    __device__ __forceinline__ void init(int w, int ln) {
+        first = w * PER;
+        lane = ln;
+    }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int kv0, const int (&pid)[4],
+                                         uint32_t slab, uint32_t goff, int L, uint32_t oob) const {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));   // keeps the slot arithmetic here instead of hoisted into live registers
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (LOADS % NW == 0 || first + i < LOADS) {
+                const int z = (first + i) * 64 + ln;
+                const int r = z / SPR, c = z % SPR, pk = r >> 4;
+                const int inpage = (r % 16) * Lds<D>::ROWB + min(c, Lds<D>::CPR - 1) * 16;
+                const int pg = pk == 0 ? pid[0] : pk == 1 ? pid[1] : pk == 2 ? pid[2] : pid[3];
+                const uint32_t off = (pg >= 0 && kv0 + r < L) ? (uint32_t)pg * slab + goff + (uint32_t)inpage : oob;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + (first + i) * 1024),
+                                                         16, off, 0, 0, 0);
+            }
+    }
+};
+
+// Keys at or below qabs - window leave the row.
+__device__ __forceinline__ void window_mask(f32x16 (&s)[2], int kv0, int qabs, int window, int lane) {
+    const int hi = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key <= qabs - window) s[t][r] = -INFINITY;
+        }
+}
+
+template <int D>
+__global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void prefill_paged_kernel(const PagedArgs a) {
+    constexpr int NW = kDenseWaves;
+    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::KTILE];
+    __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::VTILE];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int per_tile = a.B * a.Hkv * a.NHG;
+    const int pt = a.n_ptiles - 1 - (int)(blockIdx.x / per_tile);
+    int rest = (int)(blockIdx.x % per_tile);
+    const int g = rest % a.Hkv;
+    rest /= a.Hkv;
+    const int hg = rest % a.NHG;
+    const int b = rest / a.NHG;
+    const int h = g * a.G + hg * a.HPW + (w % a.HPW);
+    const int p0 = pt * a.PPW;                    // first chunk row of the work-group
+    const int r0 = p0 + 32 * (w / a.HPW);         // first chunk row of this wave
+    const int qrow = r0 + (lane & 31);
+    const int L = a.lens[b];
+    const int base = L - a.Nq;                    // position of chunk row 0
+    const int q0abs = base + r0;
+    const int qabs = q0abs + (lane & 31);
+    const int hi_key = base + min(a.Nq, p0 + a.PPW) - 1;   // latest key any row of the work-group sees
+    const int lo_key = a.window > 0 ? max(0, base + p0 - a.window + 1) : 0;
+    const int t0 = lo_key / kBN;
+    const int ntiles = hi_key >= 0 ? hi_key / kBN - t0 + 1 : 0;
+
+    const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)a.Nq * D;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.kc), (short)0, (int)a.cache_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.vc), (short)0, (int)a.cache_bytes, 0x00020000);
+
+    bf16x8 qf[D / 16];
+    load_q<D>(qf, a.q + qoff, qrow, a.Nq, lane);
+    RowState<D> st;
+    init_state<D>(st);
+
+    PagedLoader<D, NW, Lds<D>::KSTR> lk;
+    PagedLoader<D, NW, Lds<D>::VSTR> lv;
+    lk.init(w, lane);
+    lv.init(w, lane);
+    VtAddr<D> va;
+    va.init(lane);
+    const int32_t* btrow = a.bt + (size_t)b * a.max_pages;
+    const int npages = min((L + kPageTokens - 1) / kPageTokens, a.max_pages);
+    const uint32_t slab = (uint32_t)a.Hkv * kPageTokens * Lds<D>::ROWB;
+    const uint32_t goff = (uint32_t)g * kPageTokens * Lds<D>::ROWB;
+    // the tile's four pages, -1 where the table gives none
+    auto pages_of = [&](int kv0, int (&pg)[4]) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int ix = kv0 / kPageTokens + k;
+            const int pid = ix < npages ? btrow[ix] : -1;
+            pg[k] = (unsigned)pid < (unsigned)a.num_pages ? pid : -1;
+        }
+    };
+    int kv = t0 * kBN;
+    int pc[4];
+    if (ntiles > 0) {
+        pages_of(kv, pc);
+        lk.load(krs, (lds_char*)k0, kv, pc, slab, goff, L, a.cache_bytes);
+        lv.load(vrs, (lds_char*)v0, kv, pc, slab, goff, L, a.cache_bytes);
+    }
+    for (int j = 0; j < ntiles; ++j) {
+        const int kv_n = kv + kBN;
+        int pn[4] = {-1, -1, -1, -1};
+        if (j + 1 < ntiles) pages_of(kv_n, pn);
+        wait_vmem();
+        __syncthreads();
+        f32x16 sc[2];
+        uint32_t pw[2][8];
+        qk_tile<D>((lds_char*)k0, qf, sc, lane);
+        __syncthreads();   // every wave is done with K(j)
+        if (j + 1 < ntiles) lk.load(krs, (lds_char*)k0, kv_n, pn, slab, goff, L, a.cache_bytes);
+        if (a.window > 0 && kv <= q0abs + 31 - a.window) window_mask(sc, kv, qabs, a.window, lane);
+        softmax_tile<D>(sc, pw, st, a.c2, kv + kBN - 1 > q0abs, kv, qabs, lane);
+        pv_tile<D>((lds_char*)v0, va, pw, st);
+        __syncthreads();   // and with V(j)
+        if (j + 1 < ntiles) lv.load(vrs, (lds_char*)v0, kv_n, pn, slab, goff, L, a.cache_bytes);
+        kv = kv_n;
+    }
+    finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.Nq : nullptr, qrow, a.Nq, lane);
+}
+
 struct SparseArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -678,6 +829,38 @@ hipError_t launch_prefill_dense_bf16(const PrefillProblem& p, hipStream_t s) {
         hipLaunchKernelGGL((prefill_dense_kernel<128>), grid, dim3(NW * 64), 0, s, a);
     else
         hipLaunchKernelGGL((prefill_dense_kernel<64>), grid, dim3(NW * 64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_paged(const PagedPrefillProblem& p, hipStream_t s) {
+    constexpr int NW = kDenseWaves;
+    PagedArgs a;
+    a.q = static_cast<const uint16_t*>(p.q);
+    a.kc = static_cast<const uint16_t*>(p.k_cache);
+    a.vc = static_cast<const uint16_t*>(p.v_cache);
+    a.o = static_cast<uint16_t*>(p.o);
+    a.lse = p.lse;
+    a.bt = p.block_table;
+    a.lens = p.seq_lens;
+    a.B = p.B;
+    a.Hq = p.Hq;
+    a.Hkv = p.Hkv;
+    a.Nq = p.Nq;
+    a.G = p.Hq / p.Hkv;
+    a.max_pages = p.max_pages;
+    a.num_pages = p.num_pages;
+    a.window = p.window;
+    a.HPW = gcd_int(a.G, NW);
+    a.NHG = a.G / a.HPW;
+    a.PPW = 32 * (NW / a.HPW);
+    a.n_ptiles = (p.Nq + a.PPW - 1) / a.PPW;
+    a.cache_bytes = (uint32_t)p.cache_bytes;
+    a.c2 = p.scale * kLog2e;
+    const dim3 grid((unsigned)(a.n_ptiles * a.B * a.Hkv * a.NHG));
+    if (p.D == 128)
+        hipLaunchKernelGGL((prefill_paged_kernel<128>), grid, dim3(NW * 64), 0, s, a);
+    else
+        hipLaunchKernelGGL((prefill_paged_kernel<64>), grid, dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 

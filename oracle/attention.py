@@ -197,33 +197,35 @@ def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_
 
 
 def paged_prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray,
-                  seq_lens: np.ndarray, scale: float, window: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+                  seq_lens: np.ndarray, scale: float, window: int = 0,
+                  rows: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Chunked prefill over a paged cache: sequence b holds L_b = seq_lens[b] cached tokens, the last Nq of which
     are the chunk whose queries q[b, :, r] (r < Nq) sit at positions P_b + r, P_b = L_b - Nq (their own K/V are
     already in the cache). Query position p sees key t when t <= p and, with a sliding window W > 0, when
     t > p - W (its W latest keys, itself included; "Your Context Length Decides What a Kernel Is Worth" names
     sliding-window attention on half of a model's layers; "attention-kernel-optimization", section
     "PagedAttention", gives the paged layout). q [B,Hq,Nq,D]; caches [num_pages,Hkv,page,D] float64.
-    Returns O [B,Hq,Nq,D] and natural-log lse [B,Hq,Nq]."""
+    Returns O [B,Hq,R,D] and natural-log lse [B,Hq,R] for the chunk rows `rows` (all Nq when None)."""
     B, Hq, Nq, D = q.shape
     Hkv = k_cache.shape[1]
     G = _group(Hq, Hkv)
-    out = np.zeros((B, Hq, Nq, D), dtype=np.float64)
-    lse = np.full((B, Hq, Nq), -np.inf, dtype=np.float64)
+    rr = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((B, Hq, len(rr), D), dtype=np.float64)
+    lse = np.full((B, Hq, len(rr)), -np.inf, dtype=np.float64)
     for b in range(B):
         L = int(seq_lens[b])
         if L < Nq:
             raise ValueError("every sequence must hold at least the chunk's tokens")
         K = gather_paged(k_cache, block_table, b, L)
         V = gather_paged(v_cache, block_table, b, L)
-        pos = (L - Nq) + np.arange(Nq)
+        pos = (L - Nq) + rr
         t = np.arange(L)
         allowed = t[None, :] <= pos[:, None]
         if window > 0:
             allowed &= t[None, :] > pos[:, None] - window
         for h in range(Hq):
             g = h // G
-            s = scale * (q[b, h] @ K[:, g, :].T)
+            s = scale * (q[b, h, rr] @ K[:, g, :].T)
             out[b, h], lse[b, h] = _softmax_rows(s, allowed, V[:, g, :])
     return out, lse
 

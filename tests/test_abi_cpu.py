@@ -31,14 +31,14 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     decl = declared_functions()
-    assert len(decl) == 10
+    assert len(decl) == 11
     for name in decl:
         assert hasattr(L, name), name
     assert set(decl) == set(lca.EXPORTS)
 
 
 def test_version_and_status_strings(L):
-    assert lca.abi_version() == 3
+    assert lca.abi_version() == 4
     for st in range(7):
         assert L.attn_status_string(st)
     assert L.attn_status_string(99) == b"unknown status"
@@ -204,3 +204,30 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(lca.LcattnError):
         lca.prefill_dense(q, q[:, :1].contiguous(), q[:, :1].contiguous())
+
+
+def pshape(B=2, Hq=8, Hkv=2, D=128, Nq=100, page=16, maxp=64, pages=200, window=0, scale=0.1):
+    return lca.AttnPagedPrefillShape(B, Hq, Hkv, D, Nq, page, maxp, pages, window, scale)
+
+
+@pytest.mark.parametrize("s,code", [
+    (pshape(Hq=7), 2),
+    (pshape(D=96), 3),
+    (pshape(page=32), 3),
+    (pshape(window=-1), 2),
+    (pshape(Nq=-1), 2),
+    (pshape(scale=0.0), 2),
+    (pshape(Nq=64 * 16 + 1), 2),
+    (pshape(pages=0), 2),
+    (pshape(pages=1 << 20, Hkv=8), 3),      # 4 GiB per cache
+])
+def test_prefill_paged_rejects(L, s, code):
+    assert L.attn_prefill_paged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == code
+    assert L.attn_last_error()
+
+
+def test_prefill_paged_pointer_checks(L):
+    s = pshape()
+    assert L.attn_prefill_paged(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert L.attn_prefill_paged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, None) == 4
+    assert L.attn_prefill_paged(ctypes.byref(pshape(Nq=0)), None, None, None, None, None, None, None, None) == 0

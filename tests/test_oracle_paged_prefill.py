@@ -76,3 +76,13 @@ def test_equals_pure_python_loops(window):
                     want = sum(w[t] * vc[bt[b, t // 16], 0, t % 16, d] for t in keys) / tot
                     assert abs(O[b, h, r, d] - want) < 1e-12
                 assert abs(lse[b, h, r] - (mx + math.log(tot))) < 1e-12
+
+
+def test_row_subset_equals_full_rows():
+    p = W.paged_prefill_inputs(5, 2, 4, 2, 16, 40, 16, 40, 90, window=9)
+    q, kc, vc, bt, L = f64(p)
+    O, lse = A.paged_prefill(q, kc, vc, bt, L, p.scale, window=9)
+    rows = np.array([0, 7, 31, 39])
+    Os, ls = A.paged_prefill(q, kc, vc, bt, L, p.scale, window=9, rows=rows)
+    np.testing.assert_array_equal(Os, O[:, :, rows])
+    np.testing.assert_array_equal(ls, lse[:, :, rows])
