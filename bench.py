@@ -318,15 +318,17 @@ def main():
         qp, kp, vp = to_dev(p.q), to_dev(c.k_cache), to_dev(c.v_cache)
         btp, slp = torch.from_numpy(c.block_table).to(dev), torch.from_numpy(c.seq_lens).to(dev)
         op = torch.empty_like(qp)
-        log(f"paged prefill {name}")
+        wsb = lca.prefill_paged_workspace_bytes(qp, kp, btp, window=w["window"])
+        wsp = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+        log(f"paged prefill {name} (workspace {wsb} bytes)")
         t, sp = time_calls(lambda: lca.prefill_paged(qp, kp, vp, btp, slp, window=w["window"], scale=p.scale, out=op,
-                                                     return_lse=False), reps)
+                                                     return_lse=False, workspace=wsp), reps)
         Lp = c.seq_lens.astype(np.int64)
         Nq = w["Nq"]
         pos = (Lp[:, None] - Nq) + np.arange(Nq)[None, :]
         keys = np.minimum(pos + 1, w["window"]) if w["window"] > 0 else pos + 1
         fl = 4.0 * w["D"] * w["Hq"] * float(keys.sum())
-        return {"ms": t, **sp, "tflops": fl / (t * 1e-3) / 1e12, "pct_bf16_peak": 100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        return {"ms": t, **sp, "key_range_split": wsb > 0, "tflops": fl / (t * 1e-3) / 1e12, "pct_bf16_peak": 100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                 "new_tokens_per_s": w["B"] * Nq / (t * 1e-3), "flop": fl}
 
     paths["paged_prefill_c6_chunk4k_of_32k"] = paged_line("c6_paged_prefill_chunk", 20)

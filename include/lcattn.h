@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define LCATTN_ABI_VERSION 4
+#define LCATTN_ABI_VERSION 5
 
 typedef enum {
     ATTN_OK = 0,
@@ -150,17 +150,24 @@ typedef struct {
  * p = L_b - q_len + r and sees the keys t <= p, and with window > 0 only those with t > p - window. Each row is
  * exact attention over those keys with the dense prefill's arithmetic.
  *   q            bf16 [batch, heads_q, q_len, head_dim]
- *   k_cache, v_cache  bf16 [num_pages, heads_kv, page_size, head_dim]; at most 2^32 - 1 bytes each
+ *   k_cache, v_cache  bf16 [num_pages, heads_kv, page_size, head_dim]
  *   block_table  int32 [batch, max_pages_per_seq]; entries below ceil(L_b / page_size) are read (trusted, in
  *                [0, num_pages); an entry outside reads as zeros)
  *   seq_lens     int32 [batch], each in [q_len, max_pages_per_seq * page_size] (trusted)
  *   o            bf16 like q; lse optional fp32 [batch, heads_q, q_len] (NULL to skip).
+ *   workspace    device scratch of attn_prefill_paged_workspace_bytes(shape) bytes, or NULL (see there).
  * Cache slots at or past a sequence's end may hold any bits; they never reach the output. q_len 0 is a no-op.
  * Supported: head_dim 64 or 128, page_size 16.
  */
 attn_status_t attn_prefill_paged(const attn_paged_prefill_shape_t* shape, const void* q, const void* k_cache,
                                  const void* v_cache, const int32_t* block_table, const int32_t* seq_lens, void* o,
-                                 float* lse, void* stream);
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace (256-byte aligned) with which attn_prefill_paged splits each row set's keys across
+ * several work-groups and merges them by log-sum-exp: chosen from the shape when the chunk alone has too few, or
+ * too evenly loaded, work-groups to fill the GPU (a chunk closing a long sequence). 0 when no split is taken.
+ * attn_prefill_paged given less (or NULL) runs unsplit, with the same result up to rounding. */
+size_t attn_prefill_paged_workspace_bytes(const attn_paged_prefill_shape_t* shape);
 
 /* Bytes of device workspace attn_decode_paged needs when no sequence is longer than max_seq_len. */
 size_t attn_decode_workspace_bytes(const attn_decode_shape_t* shape, int32_t max_seq_len);

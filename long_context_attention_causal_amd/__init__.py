@@ -61,7 +61,8 @@ class AttnDecodeShape(ctypes.Structure):
 
 
 EXPORTS = ("attn_prefill_dense", "attn_block_mask_workspace_bytes", "attn_block_mask_build",
-           "attn_prefill_block_sparse", "attn_prefill_paged", "attn_decode_workspace_bytes", "attn_decode_paged",
+           "attn_prefill_block_sparse", "attn_prefill_paged", "attn_prefill_paged_workspace_bytes",
+           "attn_decode_workspace_bytes", "attn_decode_paged",
            "attn_decode_paged_fp8", "attn_status_string", "attn_last_error", "attn_abi_version")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -99,7 +100,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_prefill_block_sparse.restype = i32
     lib.attn_prefill_block_sparse.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.attn_prefill_paged.restype = i32
-    lib.attn_prefill_paged.argtypes = [ctypes.POINTER(AttnPagedPrefillShape), vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_prefill_paged.argtypes = [ctypes.POINTER(AttnPagedPrefillShape), vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                       vp]
+    lib.attn_prefill_paged_workspace_bytes.restype = sz
+    lib.attn_prefill_paged_workspace_bytes.argtypes = [ctypes.POINTER(AttnPagedPrefillShape)]
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(AttnDecodeShape), i32]
     lib.attn_decode_paged.restype = i32
@@ -350,7 +354,8 @@ def decode_paged_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache_t: torch.Te
 
 def prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                   seq_lens: torch.Tensor, window: int = 0, scale: Optional[float] = None,
-                  out: Optional[torch.Tensor] = None, return_lse: bool = True, stream=None
+                  out: Optional[torch.Tensor] = None, return_lse: bool = True,
+                  workspace: Optional[torch.Tensor] = None, stream=None
                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked prefill over a paged bf16 cache. q [B,Hq,Nq,D]: the last Nq of each sequence's seq_lens[b] tokens
     (already in the cache [pages,Hkv,16,D]); window 0 = causal over the whole sequence, W > 0 = the W latest keys."""
@@ -375,6 +380,21 @@ def prefill_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     o = torch.empty_like(q) if out is None else out
     _like(o, "out", q.shape, torch.bfloat16, q.device)
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if return_lse else None
+    need = int(lib.attn_prefill_paged_workspace_bytes(ctypes.byref(shp)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+        _same_device(q.device, (workspace, "workspace"))
     _check(lib.attn_prefill_paged(ctypes.byref(shp), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                                  _ptr(seq_lens), _ptr(o), _ptr(lse), _stream(stream, q.device)))
+                                  _ptr(seq_lens), _ptr(o), _ptr(lse), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel(), _stream(stream, q.device)))
     return o, lse
+
+
+def prefill_paged_workspace_bytes(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor,
+                                  window: int = 0) -> int:
+    B, Hq, Nq, D = q.shape
+    P, Hkv, page, _ = k_cache.shape
+    shp = AttnPagedPrefillShape(B, Hq, Hkv, D, Nq, page, block_table.shape[1], P, int(window), 1.0)
+    return int(load().attn_prefill_paged_workspace_bytes(ctypes.byref(shp)))

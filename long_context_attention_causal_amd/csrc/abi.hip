@@ -272,9 +272,27 @@ attn_status_t attn_decode_paged(const attn_decode_shape_t* shape, const void* q,
     return hip_status(lcattn::launch_decode_paged(p, workspace, static_cast<hipStream_t>(stream)), "attn_decode_paged");
 }
 
+namespace {
+
+int paged_splits(const attn_paged_prefill_shape_t& s) {
+    return lcattn::paged_prefill_splits(s.batch, s.heads_q, s.heads_kv, s.head_dim, s.q_len,
+                                        s.max_pages_per_seq * s.page_size, s.window);
+}
+
+}  // namespace
+
+size_t attn_prefill_paged_workspace_bytes(const attn_paged_prefill_shape_t* shape) {
+    if (!shape || shape->batch < 1 || shape->heads_q < 1 || shape->heads_kv < 1 || shape->q_len < 0 ||
+        shape->max_pages_per_seq < 1 || shape->window < 0 || shape->heads_q % shape->heads_kv ||
+        (shape->head_dim != 64 && shape->head_dim != 128) || shape->page_size != 16)
+        return 0;
+    return lcattn::paged_prefill_workspace_bytes(shape->batch, shape->heads_q, shape->head_dim, shape->q_len,
+                                                 paged_splits(*shape));
+}
+
 attn_status_t attn_prefill_paged(const attn_paged_prefill_shape_t* shape, const void* q, const void* k_cache,
                                  const void* v_cache, const int32_t* block_table, const int32_t* seq_lens, void* o,
-                                 float* lse, void* stream) {
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
     if (!shape) return fail(ATTN_ERR_NULL, "shape is NULL");
     const attn_paged_prefill_shape_t& s = *shape;
     if (s.batch < 1 || s.heads_q < 1 || s.heads_kv < 1 || s.q_len < 0 || s.num_pages < 0 || s.max_pages_per_seq < 1 ||
@@ -286,9 +304,6 @@ attn_status_t attn_prefill_paged(const attn_paged_prefill_shape_t* shape, const 
     if (!(std::isfinite(s.scale) && s.scale > 0.0f)) return fail(ATTN_ERR_SHAPE, "scale must be finite and > 0");
     if ((long long)s.q_len > (long long)s.max_pages_per_seq * s.page_size)
         return fail(ATTN_ERR_SHAPE, "q_len exceeds max_pages_per_seq * page_size");
-    const unsigned long long cache_bytes =
-        (unsigned long long)s.num_pages * s.heads_kv * s.page_size * s.head_dim * 2ull;
-    if (cache_bytes > 0xFFFFFFFFull) return fail(ATTN_ERR_UNSUPPORTED, "a cache above 2^32 - 1 bytes");
     // work-groups: ceil(q_len / positions per group) x batch x kv heads x head groups <= (q_len / 32 + 1) x batch x heads_q
     if (((long long)s.q_len / 32 + 1) * s.batch * s.heads_q > 0x7FFFFFFFLL)
         return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
@@ -313,8 +328,14 @@ attn_status_t attn_prefill_paged(const attn_paged_prefill_shape_t* shape, const 
     p.max_pages = s.max_pages_per_seq;
     p.num_pages = s.num_pages;
     p.window = s.window;
-    p.cache_bytes = (size_t)cache_bytes;
     p.scale = s.scale;
+    // key-range splits need their workspace; without it (NULL or too small) the chunk runs unsplit
+    p.splits = paged_splits(s);
+    const size_t need = lcattn::paged_prefill_workspace_bytes(s.batch, s.heads_q, s.head_dim, s.q_len, p.splits);
+    if (p.splits > 1 && (!workspace || workspace_bytes < need)) p.splits = 1;
+    if (p.splits > 1 && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(ATTN_ERR_ALIGN, "workspace must be 256-byte aligned");
+    p.workspace = workspace;
     return hip_status(lcattn::launch_prefill_paged(p, static_cast<hipStream_t>(stream)), "attn_prefill_paged");
 }
 

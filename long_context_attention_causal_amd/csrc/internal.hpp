@@ -73,10 +73,13 @@ struct PagedPrefillProblem {
     void* o;
     float* lse;  // may be null
     int B, Hq, Hkv, D, Nq, max_pages, num_pages, window;
-    size_t cache_bytes;   // bytes of one cache, below 2^32
     float scale;
+    int splits;           // key-range splits (1: no workspace)
+    void* workspace;      // splits > 1: paged_prefill_workspace_bytes
 };
 hipError_t launch_prefill_paged(const PagedPrefillProblem& p, hipStream_t s);
+int paged_prefill_splits(int B, int Hq, int Hkv, int D, int Nq, int max_seq_len, int window);
+size_t paged_prefill_workspace_bytes(int B, int Hq, int D, int Nq, int splits);
 
 size_t decode_workspace_bytes(int B, int Hq, int D, int chunk, int max_seq_len);
 hipError_t launch_decode_paged(const DecodeProblem& p, void* workspace, hipStream_t s);

@@ -517,43 +517,95 @@ struct PagedArgs {
     const int32_t* lens;
     int B, Hq, Hkv, Nq, G, max_pages, num_pages, window;
     int HPW, NHG, PPW, n_ptiles;
-    uint32_t cache_bytes;   // bytes of one cache: the buffer view's size
     float c2;
+    int splits;             // work-groups sharing one row set's key tiles (gridDim.y); 1 writes O directly
+    float* opart;           // splits > 1: [splits, B, Hq, Nq, D] normalised partial outputs
+    float* lpart;           // splits > 1: [splits, B, Hq, Nq] their natural-log lse
 };
 
-// Gathering tile loader: a 64-key tile spans four 16-token pages, and each 16-byte LDS slot's source row is read
-// from its page (one slab of 16 x D per page and kv head). Slots of keys at or past the sequence end, or on a page
-// the table does not give, point past the view and read zeros.
-// The slot's row and source offset are recomputed per load (a few integer operations) rather than kept, which
-// holds the kernel inside three waves' register budget.
-template <int D, int NW, int STR>
-struct PagedLoader {
-    static constexpr int LOADS = kBN * STR / 1024;
-    static constexpr int PER = (LOADS + NW - 1) / NW;
-    static constexpr int SPR = STR / 16;
-    int first;   // this wave's first load slot
-    int lane;
-    __device__ __forceinline__ void init(int w, int ln) {
-        first = w * PER;
-        lane = ln;
-    }
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int kv0, const int (&pid)[4],
-                                         uint32_t slab, uint32_t goff, int L, uint32_t oob) const {
-        int ln = lane;
-        asm volatile("" : "+v"(ln));   // keeps the slot arithmetic here instead of hoisted into live registers
+// A split's rows: the output normalised by the split's own sum, and the split's lse (-inf with no key).
+template <int D>
+__device__ __forceinline__ void finish_partial(const RowState<D>& st, float* orow_base, float* lrow, int qrow, int N,
+                                               int lane) {
+    const int hi = lane >> 5;
+    const float lt = pair_sum(st.l);
+    if (qrow >= N) return;
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    float* orow = orow_base + (size_t)qrow * D;
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (LOADS % NW == 0 || first + i < LOADS) {
-                const int z = (first + i) * 64 + ln;
-                const int r = z / SPR, c = z % SPR, pk = r >> 4;
-                const int inpage = (r % 16) * Lds<D>::ROWB + min(c, Lds<D>::CPR - 1) * 16;
-                const int pg = pk == 0 ? pid[0] : pk == 1 ? pid[1] : pk == 2 ? pid[2] : pid[3];
-                const uint32_t off = (pg >= 0 && kv0 + r < L) ? (uint32_t)pg * slab + goff + (uint32_t)inpage : oob;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + (first + i) * 1024),
-                                                         16, off, 0, 0, 0);
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int d0 = 32 * dt + 8 * a + 4 * hi;
+            f32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = st.o[dt][4 * a + j] * inv;
+            *reinterpret_cast<f32x4*>(orow + d0) = v;
+        }
+    if (hi == 0) lrow[qrow] = lt > 0.0f ? (st.m + log2f(lt)) * kLn2 : -INFINITY;
+}
+
+// Page loads: with four waves and 64-key tiles each wave stages exactly one 16-token page of K and one of V. The
+// wave builds one buffer view per page (64-bit base at the page's slab, size clipped at the sequence end, so rows
+// past it and pages the table does not give read zeros) and issues whole 1 KiB direct-to-LDS loads whose per-lane
+// source offsets inside the slab never change. K pages land in an unpadded, XOR-swizzled layout (a page is then a
+// whole number of loads): 16-byte chunk c of row r sits at chunk c ^ swz(r), which spreads any 16 consecutive rows'
+// reads of one chunk over all banks. V keeps the dense kernel's padded layout, whose pages are whole loads already.
+template <int D>
+struct SwzK {
+    static constexpr int ROWB = D * 2;
+    static constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+    static constexpr int RPL = 256 / ROWB;         // rows per 256-byte bank line
+    static constexpr int TILE = kBN * ROWB;
+    __device__ __forceinline__ static int swz(int r) { return (r / RPL) & (CPR - 1); }
+};
+
+template <int D, int ROWSTR, bool SWZ>
+struct PageLoader {
+    static constexpr int ROWB = D * 2;
+    static constexpr int CPR = ROWB / 16;
+    static constexpr int PAGEB = kPageTokens * ROWSTR;   // LDS bytes of one page
+    static constexpr int LPP = PAGEB / 1024;             // 1 KiB loads per page
+    static_assert(PAGEB % 1024 == 0, "a page must be whole direct loads");
+    int voff[LPP];
+    __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+        for (int j = 0; j < LPP; ++j) {
+            const int z = j * 64 + lane;   // 16-byte slot inside the page's LDS image
+            if constexpr (SWZ) {
+                const int r = z / CPR, cl = z % CPR;
+                voff[j] = r * ROWB + (cl ^ SwzK<D>::swz(r)) * 16;
+            } else {
+                constexpr int SPR = ROWSTR / 16;
+                const int r = z / SPR, c = z % SPR;
+                voff[j] = r * ROWB + min(c, CPR - 1) * 16;   // a padding slot re-reads a chunk of its row
             }
+        }
+    }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t page, lds_char* tile, int w) const {
+#pragma unroll
+        for (int j = 0; j < LPP; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                page, (__attribute__((address_space(3))) void*)(tile + w * PAGEB + j * 1024), 16, voff[j], 0, 0, 0);
     }
 };
+
+// S^T of a 64-key tile from the swizzled K layout (the same result as qk_tile).
+template <int D>
+__device__ __forceinline__ void qk_tile_swz(const lds_char* kl, const bf16x8 (&qf)[D / 16], f32x16 (&s)[2], int lane) {
+    const int hi = lane >> 5, ln = lane & 31;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int r = 32 * t + ln;
+            const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                kl + r * SwzK<D>::ROWB + (((2 * ks + hi) ^ SwzK<D>::swz(r)) * 16));
+            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
+        }
+}
 
 // Keys at or below qabs - window leave the row.
 __device__ __forceinline__ void window_mask(f32x16 (&s)[2], int kv0, int qabs, int window, int lane) {
@@ -571,7 +623,8 @@ template <int D>
 __global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void prefill_paged_kernel(const PagedArgs a) {
     constexpr int NW = kDenseWaves;
-    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::KTILE];
+    static_assert(NW * kPageTokens == kBN, "one page per wave");
+    __shared__ __attribute__((aligned(1024))) char k0[SwzK<D>::TILE];
     __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::VTILE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -592,65 +645,110 @@ void prefill_paged_kernel(const PagedArgs a) {
     const int qabs = q0abs + (lane & 31);
     const int hi_key = base + min(a.Nq, p0 + a.PPW) - 1;   // latest key any row of the work-group sees
     const int lo_key = a.window > 0 ? max(0, base + p0 - a.window + 1) : 0;
-    const int t0 = lo_key / kBN;
-    const int ntiles = hi_key >= 0 ? hi_key / kBN - t0 + 1 : 0;
+    const int t_first = lo_key / kBN;
+    const int ntiles_all = hi_key >= 0 ? hi_key / kBN - t_first + 1 : 0;
+    // this work-group's share of the tiles: split blockIdx.y of gridDim.y
+    const int per_split = (ntiles_all + a.splits - 1) / a.splits;
+    const int t0 = t_first + (int)blockIdx.y * per_split;
+    const int ntiles = max(0, min(per_split, ntiles_all - (int)blockIdx.y * per_split));
 
     const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)a.Nq * D;
-    const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.kc), (short)0, (int)a.cache_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.vc), (short)0, (int)a.cache_bytes, 0x00020000);
 
     bf16x8 qf[D / 16];
     load_q<D>(qf, a.q + qoff, qrow, a.Nq, lane);
     RowState<D> st;
     init_state<D>(st);
 
-    PagedLoader<D, NW, Lds<D>::KSTR> lk;
-    PagedLoader<D, NW, Lds<D>::VSTR> lv;
-    lk.init(w, lane);
-    lv.init(w, lane);
+    PageLoader<D, SwzK<D>::ROWB, true> lk;
+    PageLoader<D, Lds<D>::VSTR, false> lv;
+    lk.init(lane);
+    lv.init(lane);
     VtAddr<D> va;
     va.init(lane);
     const int32_t* btrow = a.bt + (size_t)b * a.max_pages;
     const int npages = min((L + kPageTokens - 1) / kPageTokens, a.max_pages);
-    const uint32_t slab = (uint32_t)a.Hkv * kPageTokens * Lds<D>::ROWB;
-    const uint32_t goff = (uint32_t)g * kPageTokens * Lds<D>::ROWB;
-    // the tile's four pages, -1 where the table gives none
-    auto pages_of = [&](int kv0, int (&pg)[4]) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int ix = kv0 / kPageTokens + k;
-            const int pid = ix < npages ? btrow[ix] : -1;
-            pg[k] = (unsigned)pid < (unsigned)a.num_pages ? pid : -1;
+    // this wave's page of the tile starting at key kv0: K and V views clipped at the sequence end
+    auto views = [&](int kv0, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr) {
+        const int ix = kv0 / kPageTokens + w;
+        int pid = ix < npages ? btrow[ix] : -1;
+        int valid = min(kPageTokens, L - ix * kPageTokens);
+        if ((unsigned)pid >= (unsigned)a.num_pages || valid <= 0) {
+            pid = 0;
+            valid = 0;
         }
+        const size_t slab = ((size_t)pid * a.Hkv + g) * (size_t)(kPageTokens * D);
+        kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.kc + slab), (short)0, valid * D * 2, 0x00020000);
+        vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.vc + slab), (short)0, valid * D * 2, 0x00020000);
     };
     int kv = t0 * kBN;
-    int pc[4];
     if (ntiles > 0) {
-        pages_of(kv, pc);
-        lk.load(krs, (lds_char*)k0, kv, pc, slab, goff, L, a.cache_bytes);
-        lv.load(vrs, (lds_char*)v0, kv, pc, slab, goff, L, a.cache_bytes);
+        __amdgpu_buffer_rsrc_t kr, vr;
+        views(kv, kr, vr);
+        lk.load(kr, (lds_char*)k0, w);
+        lv.load(vr, (lds_char*)v0, w);
     }
     for (int j = 0; j < ntiles; ++j) {
         const int kv_n = kv + kBN;
-        int pn[4] = {-1, -1, -1, -1};
-        if (j + 1 < ntiles) pages_of(kv_n, pn);
+        __amdgpu_buffer_rsrc_t kn, vn;
+        views(kv_n, kn, vn);   // past the last tile this is an empty view and is not used
         wait_vmem();
         __syncthreads();
         f32x16 sc[2];
         uint32_t pw[2][8];
-        qk_tile<D>((lds_char*)k0, qf, sc, lane);
+        qk_tile_swz<D>((lds_char*)k0, qf, sc, lane);
         __syncthreads();   // every wave is done with K(j)
-        if (j + 1 < ntiles) lk.load(krs, (lds_char*)k0, kv_n, pn, slab, goff, L, a.cache_bytes);
+        if (j + 1 < ntiles) lk.load(kn, (lds_char*)k0, w);
         if (a.window > 0 && kv <= q0abs + 31 - a.window) window_mask(sc, kv, qabs, a.window, lane);
         softmax_tile<D>(sc, pw, st, a.c2, kv + kBN - 1 > q0abs, kv, qabs, lane);
         pv_tile<D>((lds_char*)v0, va, pw, st);
         __syncthreads();   // and with V(j)
-        if (j + 1 < ntiles) lv.load(vrs, (lds_char*)v0, kv_n, pn, slab, goff, L, a.cache_bytes);
+        if (j + 1 < ntiles) lv.load(vn, (lds_char*)v0, w);
         kv = kv_n;
     }
-    finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.Nq : nullptr, qrow, a.Nq, lane);
+    if (a.splits == 1) {
+        finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.Nq : nullptr, qrow, a.Nq, lane);
+    } else {
+        const size_t prow = ((size_t)blockIdx.y * a.B + b) * a.Hq + h;   // (split, b, h)
+        finish_partial<D>(st, a.opart + prow * a.Nq * D, a.lpart + prow * a.Nq, qrow, a.Nq, lane);
+    }
+}
+
+// Merge of the key-range splits: one wave per (b, h, row), lane i holding D / 64 head dims.
+struct PagedCombineArgs {
+    const float* opart;
+    const float* lpart;
+    uint16_t* o;
+    float* lse;
+    long rows;    // B * Hq * Nq
+    int splits;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_paged_combine_kernel(const PagedCombineArgs a) {
+    constexpr int PER = D / 64;
+    const int lane = threadIdx.x & 63;
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= a.rows) return;
+    float M = -INFINITY;
+    for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, a.lpart[sp * a.rows + row]);
+    float acc[PER] = {};
+    float wsum = 0.0f;
+    for (int sp = 0; sp < a.splits; ++sp) {
+        const float ls = a.lpart[sp * a.rows + row];
+        const float w = ls == -INFINITY ? 0.0f : __expf(ls - M);
+        wsum += w;
+        const float* src = a.opart + ((size_t)sp * a.rows + row) * D + PER * lane;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] += w * src[j];
+    }
+    const float inv = 1.0f / wsum;
+    uint16_t* dst = a.o + (size_t)row * D + PER * lane;
+    if constexpr (PER == 2) {
+        *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+        dst[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.0f) & 0xFFFFu);
+    }
+    if (a.lse && lane == 0) a.lse[row] = M + __logf(wsum);
 }
 
 struct SparseArgs {
@@ -854,14 +952,59 @@ hipError_t launch_prefill_paged(const PagedPrefillProblem& p, hipStream_t s) {
     a.NHG = a.G / a.HPW;
     a.PPW = 32 * (NW / a.HPW);
     a.n_ptiles = (p.Nq + a.PPW - 1) / a.PPW;
-    a.cache_bytes = (uint32_t)p.cache_bytes;
     a.c2 = p.scale * kLog2e;
-    const dim3 grid((unsigned)(a.n_ptiles * a.B * a.Hkv * a.NHG));
+    a.splits = p.splits;
+    a.opart = static_cast<float*>(p.workspace);
+    a.lpart = a.opart + (size_t)p.splits * p.B * p.Hq * p.Nq * p.D;
+    const dim3 grid((unsigned)(a.n_ptiles * a.B * a.Hkv * a.NHG), (unsigned)p.splits);
     if (p.D == 128)
         hipLaunchKernelGGL((prefill_paged_kernel<128>), grid, dim3(NW * 64), 0, s, a);
     else
         hipLaunchKernelGGL((prefill_paged_kernel<64>), grid, dim3(NW * 64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    PagedCombineArgs c;
+    c.opart = a.opart;
+    c.lpart = a.lpart;
+    c.o = static_cast<uint16_t*>(p.o);
+    c.lse = p.lse;
+    c.rows = (long)p.B * p.Hq * p.Nq;
+    c.splits = p.splits;
+    const dim3 g2((unsigned)((c.rows + 3) / 4));
+    if (p.D == 128) hipLaunchKernelGGL((prefill_paged_combine_kernel<128>), g2, dim3(256), 0, s, c);
+    else hipLaunchKernelGGL((prefill_paged_combine_kernel<64>), g2, dim3(256), 0, s, c);
     return hipGetLastError();
+}
+
+// Key-range splits for a chunk closing a long sequence: its work-groups all carry about the same number of tiles,
+// so when there are too few of them to fill the last round the CUs idle for most of it. Each row set's tiles are
+// then shared by `splits` work-groups, chosen to minimise rounds x tiles per work-group on 256 CUs at three
+// work-groups each, counting a split only where every piece keeps at least 16 tiles. Chunks that are most of their
+// sequence (Nq > half the longest) have causal, uneven work that heaviest-first issue already spreads, and
+// windowed chunks have a few tiles per work-group: neither is split.
+int paged_prefill_splits(int B, int Hq, int Hkv, int D, int Nq, int max_seq_len, int window) {
+    constexpr int NW = kDenseWaves, kSlots = 256 * 3;
+    (void)D;
+    if (window > 0 || 2 * (long)Nq > max_seq_len) return 1;
+    const int G = Hq / Hkv, HPW = gcd_int(G, NW), PPW = 32 * (NW / HPW);
+    const long wgs = (long)((Nq + PPW - 1) / PPW) * B * Hkv * (G / HPW);
+    const int tiles = (max_seq_len + kBN - 1) / kBN + 1;
+    int best = 1;
+    double best_cost = (double)((wgs + kSlots - 1) / kSlots) * tiles;
+    for (int sp = 2; sp <= 8; ++sp) {
+        if (tiles / sp < 16) break;
+        const double cost = (double)((wgs * sp + kSlots - 1) / kSlots) * ((tiles + sp - 1) / sp) * 1.03;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = sp;
+        }
+    }
+    return best;
+}
+
+size_t paged_prefill_workspace_bytes(int B, int Hq, int D, int Nq, int splits) {
+    if (splits <= 1) return 0;
+    return (size_t)splits * B * Hq * Nq * (D + 1) * sizeof(float);
 }
 
 hipError_t launch_prefill_sparse_bf16(const PrefillProblem& p, int block, const int32_t* kv_count,

@@ -31,14 +31,14 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     decl = declared_functions()
-    assert len(decl) == 11
+    assert len(decl) == 12
     for name in decl:
         assert hasattr(L, name), name
     assert set(decl) == set(lca.EXPORTS)
 
 
 def test_version_and_status_strings(L):
-    assert lca.abi_version() == 4
+    assert lca.abi_version() == 5
     for st in range(7):
         assert L.attn_status_string(st)
     assert L.attn_status_string(99) == b"unknown status"
@@ -219,15 +219,27 @@ def pshape(B=2, Hq=8, Hkv=2, D=128, Nq=100, page=16, maxp=64, pages=200, window=
     (pshape(scale=0.0), 2),
     (pshape(Nq=64 * 16 + 1), 2),
     (pshape(pages=0), 2),
-    (pshape(pages=1 << 20, Hkv=8), 3),      # 4 GiB per cache
 ])
 def test_prefill_paged_rejects(L, s, code):
-    assert L.attn_prefill_paged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == code
+    assert L.attn_prefill_paged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == code
     assert L.attn_last_error()
 
 
 def test_prefill_paged_pointer_checks(L):
     s = pshape()
-    assert L.attn_prefill_paged(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None) == 1
-    assert L.attn_prefill_paged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, None) == 4
-    assert L.attn_prefill_paged(ctypes.byref(pshape(Nq=0)), None, None, None, None, None, None, None, None) == 0
+    assert L.attn_prefill_paged(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
+    assert L.attn_prefill_paged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, None, 0, None) == 4
+    assert L.attn_prefill_paged(ctypes.byref(pshape(Nq=0)), None, None, None, None, None, None, None, None, 0,
+                                None) == 0
+
+
+def test_prefill_paged_workspace_policy(L):
+    """A chunk closing a long sequence is split (its work-groups are too few and too even); a whole short
+    sequence or a windowed chunk is not; the workspace holds the fp32 partials and their lse."""
+    long_chunk = pshape(B=1, Hq=32, Hkv=4, D=128, Nq=4096, maxp=2048, pages=2048)
+    need = L.attn_prefill_paged_workspace_bytes(ctypes.byref(long_chunk))
+    assert need > 0 and need % (1 * 32 * 4096 * 129 * 4) == 0
+    assert L.attn_prefill_paged_workspace_bytes(ctypes.byref(pshape(Nq=4096, maxp=256, pages=256))) == 0
+    windowed = pshape(B=8, Hq=64, Hkv=8, D=64, Nq=2048, maxp=1024, pages=8000, window=128)
+    assert L.attn_prefill_paged_workspace_bytes(ctypes.byref(windowed)) == 0
+    assert L.attn_prefill_paged_workspace_bytes(ctypes.byref(pshape(D=96))) == 0

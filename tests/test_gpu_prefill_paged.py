@@ -87,3 +87,28 @@ def test_whole_sequence_equals_dense_kernel_bitwise(lib, D, N):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
     assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("D,Nq,lens", [(128, 256, [4096]), (64, 200, [3000, 700]), (128, 96, [2500, 96, 1200])])
+def test_key_range_split_matches_oracle_and_unsplit(lib, D, Nq, lens):
+    """Chunks closing long sequences take the key-range split (a workspace is allocated); with a one-byte
+    workspace the same call runs unsplit. Both match the oracle, and each other within rounding; a sequence whose
+    chunk is all of it leaves later splits empty (their lse is -inf and they carry no weight)."""
+    p = W.paged_prefill_inputs(64, len(lens), 8, 2, D, Nq, 16, Nq, max(lens), seq_lens=np.array(lens))
+    c = p.cache
+    args = (dev_bf16(p.q), dev_bf16(c.k_cache), dev_bf16(c.v_cache), dev_i32(c.block_table), dev_i32(c.seq_lens))
+    q_dev = args[0]
+    need = lib.prefill_paged_workspace_bytes(q_dev, args[1], args[3])
+    assert need > 0, "this shape is meant to take the split"
+    o_split, l_split = lib.prefill_paged(*args, scale=p.scale)
+    tiny = torch.empty(1, dtype=torch.uint8, device=q_dev.device)
+    o_one, l_one = lib.prefill_paged(*args, scale=p.scale, workspace=tiny)
+    torch.cuda.synchronize()
+    Oref, Lref = A.paged_prefill(W.f64_from_bf16_bits(p.q), W.f64_from_bf16_bits(c.k_cache),
+                                 W.f64_from_bf16_bits(c.v_cache), c.block_table, c.seq_lens,
+                                 float(np.float32(p.scale)))
+    for o, l, tag in ((o_split, l_split, "split"), (o_one, l_one, "unsplit")):
+        eo, el = max_err(host64(o), Oref), max_err(host64(l), Lref)
+        say(f"[paged prefill] {tag} D{D} Nq{Nq} L{lens}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+        assert eo <= BF16_TOL and el <= LSE_TOL
+    assert (o_split.float() - o_one.float()).abs().max().item() <= BF16_TOL
