@@ -169,14 +169,17 @@ def test_sparse_all_blocks_equals_dense(lib, block):
     assert (lse - ld).abs().max().item() <= 1e-3
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("name", ["c3_sparse_bf16_n32k", "c4_sparse_bf16_n128k"])
-def test_sparse_full_size_sampled(lib, name):
+def test_sparse_full_size_sampled(lib, name, mode):
+    """The sparse kernel over the oracle's lists at full size, for the query-blind and the query-aware rescue."""
     w = W.WORKLOADS[name]
-    say(f"[sparse] {name}: generating inputs")
+    say(f"[sparse] {name} mode {mode}: generating inputs")
     inp = W.planted_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["block"])
     q, k, v = inp.as_f64()
-    say(f"[sparse] {name}: oracle mask")
-    ref = M.build_mask(q, k, inp.scale, w["block"], w["keep_permille"], w["alpha"], w["q_lo_pct"], w["q_hi_pct"])
+    say(f"[sparse] {name} mode {mode}: oracle mask")
+    ref = M.build_mask(q, k, inp.scale, w["block"], w["keep_permille"], w["alpha"], w["q_lo_pct"], w["q_hi_pct"],
+                       rescue_mode=mode)
     del q
     say(f"[sparse] {name}: gpu")
     o, lse = run_sparse(lib, inp, ref.kv_count, ref.kv_index)
@@ -197,7 +200,7 @@ def test_sparse_full_size_sampled(lib, name):
                                       rows=rows[h])
         Oref[:, h], Lref[:, h] = o_h[:, 0], l_h[:, 0]
     eo, el = max_err(og, Oref), max_err(lg, Lref)
-    say(f"[sparse] {name}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    say(f"[sparse] {name} mode {mode}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
     assert eo <= BF16_TOL and el <= LSE_TOL
 
 
