@@ -10,7 +10,7 @@ A step runs every variant once, each on its own synthetic workload, with inputs 
 After the timed steps the decode workload is also run over an fp8 (E4M3) copy of its cache, chunked prefill over a
 paged cache is timed (a 4K chunk closing a 32K sequence; a 128-token-window chunk over 8 sequences), and the
 long-context lines are measured on their own: dense prefill at 32K and 128K and the
-128K mask + sparse pass (speedup over this build's dense kernel at the same length), and at 32K and 128K the mask
+128K mask + sparse pass (speedup over the library's own dense kernel at the same length), and at 32K and 128K the mask
 built with the query-aware rescue (rescue_mode 1) and the sparse pass over it. The fp64 CPU oracle is timed
 on the host (cpu_baseline) on the headline workload. One JSON line goes to stdout.
 """

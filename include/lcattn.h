@@ -39,7 +39,7 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,         /* a required pointer is NULL                                        */
     ATTN_ERR_SHAPE = 2,        /* inconsistent or out-of-range sizes                                */
-    ATTN_ERR_UNSUPPORTED = 3,  /* valid request this build does not implement (dtype, head_dim ...) */
+    ATTN_ERR_UNSUPPORTED = 3,  /* valid request the library does not implement (dtype, head_dim ...) */
     ATTN_ERR_ALIGN = 4,        /* a base pointer is not 16-byte aligned                             */
     ATTN_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the *_workspace_bytes query        */
     ATTN_ERR_HIP = 6           /* the HIP runtime reported an error while enqueueing                */

@@ -127,8 +127,8 @@ def e4m3_value(codes: np.ndarray) -> np.ndarray:
     """Values of 8-bit E4M3 codes as float64, per the OCP 8-bit floating point specification (OFP8): sign bit,
     4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the subnormals M/8 * 2^-6; there are no
     infinities and S.1111.111 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448. The pages ask for an
-    fp8 KV cache ("Your Context Length Decides What a Kernel Is Worth": moving fewer bytes through the
-    --kv-cache-dtype fp8 setting) without naming the encoding; E4M3 is read as that encoding."""
+    fp8 KV cache ("Your Context Length Decides What a Kernel Is Worth": the --kv-cache-dtype fp8 setting cuts the
+    bytes decode has to read) without naming the encoding; E4M3 is read as that encoding."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     sign = np.where(c >> 7, -1.0, 1.0)
     e = (c >> 3) & 15

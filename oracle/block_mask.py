@@ -17,7 +17,7 @@ the method in outline; the steps below are its order, with the open points fixed
  5. Centroid branch: for query block i of head h, the candidates are the causally visible key blocks j <= i;
     their score is scale * <mean q-block, key centroid>; the k_i = ceil((i+1) * keep_permille / 1000) best are
     kept (integer ceiling), ties broken towards the smaller j.
- 6. The two branches are thresholded independently and OR-ed, and the diagonal block is always kept:
+ 6. Each branch applies its own threshold, the two results are OR-ed, and the diagonal block is always kept:
     M[h,i,j] = 1 iff j <= i and (centroid-kept or rescued or j == i).
  7. The kept list of each (h, i) row, ascending in j, is the CSR form the sparse kernel walks.
 
