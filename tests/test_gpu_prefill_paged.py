@@ -46,6 +46,10 @@ def compare(lib, p, label, rows=None):
     (2, 8, 2, 128, 150, [160, 701], 100),
     (2, 8, 2, 128, 150, [150, 700], 1000),
     (2, 64, 8, 64, 300, [2000, 3001], 128),
+    (3, 8, 2, 64, 1, [1, 17, 999], 0),           # one-token chunks
+    (2, 8, 2, 128, 64, [64, 1024], 1),           # window 1 at tile boundaries
+    (1, 4, 1, 64, 40, [4096], 1),                # window 1, head_dim 64
+    (2, 8, 2, 64, 70, [512, 70], 20),            # window narrower than a 32-row slice
 ])
 def test_small(lib, B, Hq, Hkv, D, Nq, lens, window):
     p = W.paged_prefill_inputs(61, B, Hq, Hkv, D, Nq, 16, Nq, max(lens), window=window, seq_lens=np.array(lens))
@@ -112,3 +116,22 @@ def test_key_range_split_matches_oracle_and_unsplit(lib, D, Nq, lens):
         say(f"[paged prefill] {tag} D{D} Nq{Nq} L{lens}: max|dO|={eo:.3e} max|dlse|={el:.3e}")
         assert eo <= BF16_TOL and el <= LSE_TOL
     assert (o_split.float() - o_one.float()).abs().max().item() <= BF16_TOL
+
+
+def test_one_token_chunk_matches_decode_kernel(lib):
+    """A one-token chunk is a decode step: the paged prefill and the split-KV decode kernel agree within rounding."""
+    p = W.paged_prefill_inputs(65, 4, 16, 2, 64, 1, 16, 1, 3000, seq_lens=np.array([1, 16, 1500, 3000]))
+    c = p.cache
+    o, lse = run(lib, p)
+    od, ld = lib.decode_paged(dev_bf16(p.q[:, :, 0]), dev_bf16(c.k_cache), dev_bf16(c.v_cache), dev_i32(c.block_table),
+                              dev_i32(c.seq_lens), 3000, scale=p.scale)
+    torch.cuda.synchronize()
+    assert (o[:, :, 0].float() - od.float()).abs().max().item() <= BF16_TOL
+    assert (lse[:, :, 0] - ld).abs().max().item() <= LSE_TOL
+
+
+def test_sequence_filling_its_block_table(lib):
+    """seq_len equal to max_pages_per_seq * page_size: the last page is full and the table has no spare entry."""
+    p = W.paged_prefill_inputs(66, 1, 8, 2, 128, 96, 16, 1024, 1024)
+    assert p.cache.block_table.shape[1] * 16 == 1024 and int(p.cache.seq_lens[0]) == 1024
+    compare(lib, p, "full block table")
