@@ -334,6 +334,24 @@ def main():
     paths["paged_prefill_c6_chunk4k_of_32k"] = paged_line("c6_paged_prefill_chunk", 20)
     paths["paged_prefill_c7_window128"] = paged_line("c7_paged_prefill_window", 20)
 
+    def fp8_key_mask(q, k_bits, w, scale, m_bf16, planted, reps):
+        """The same mask built from per-tensor E4M3 codes of the keys: its time, density, planted recall and its
+        Jaccard overlap with the bf16-key mask (kept pairs in both over kept pairs in either)."""
+        codes, ksc = W.e4m3_keys(k_bits)
+        kc = torch.from_numpy(codes).to(dev)
+        blk, nbq = w["block"], w["N"] // w["block"]
+        mk = lambda out=None: lca.block_mask_build(q, kc, blk, w["keep_permille"], w["alpha"], w["q_lo_pct"],
+                                                   w["q_hi_pct"], scale=scale, want_radius_stats=False, outputs=out,
+                                                   k_scale=ksc)
+        m = mk()
+        t, st = time_calls(lambda: mk(m), reps)
+        inter = int((m.mask & m_bf16.mask).sum().item())
+        union = int((m.mask | m_bf16.mask).sum().item())
+        cnt = m.kv_count.cpu().numpy().astype(np.int64)
+        return {"mask_ms": t, "mask_ms_median": st["ms_median"], "k_scale": ksc,
+                "density": float(cnt.sum() / (w["Hq"] * nbq * (nbq + 1) / 2)),
+                "jaccard_vs_bf16_keys": inter / union, "planted_kept": planted_kept(m.mask, planted, blk)}
+
     if not args.no_long:
         log("dense prefill at 32K")
         t32, s32 = time_calls(lambda: lca.prefill_dense(q3, k3, v3, scale=c3.scale, out=o3, return_lse=False),
@@ -346,6 +364,9 @@ def main():
         log("query-aware rescue at 32K")
         paths["sparse_prefill_n32768_b64"]["query_aware_rescue"] = query_aware(
             q3, k3, v3, o3, w3, c3.scale, t32, c3.planted, max(args.long_reps, 5))
+        log("mask from fp8 keys at 32K")
+        paths["mask_build_n32768_b64"]["fp8_keys"] = fp8_key_mask(q3, c3.k, w3, c3.scale, m3, c3.planted,
+                                                                  max(args.long_reps, 5))
         del q3, k3, v3, o3, m3
         torch.cuda.empty_cache()
         log("generating the 128K block-sparse workload")
@@ -354,6 +375,7 @@ def main():
         q4, k4, v4 = to_dev(c4.q), to_dev(c4.k), to_dev(c4.v)
         o4 = torch.empty_like(q4)
         planted4 = c4.planted
+        k4_bits = c4.k
         del c4
         log("dense prefill at 128K")
         t128, s128 = time_calls(lambda: lca.prefill_dense(q4, k4, v4, scale=1 / math.sqrt(128), out=o4,
@@ -383,7 +405,10 @@ def main():
             "speedup_vs_dense_kernel_only": t128 / ts4,
             "speedup_vs_dense_incl_mask": t128 / (ts4 + tm4),
             "planted_kept": planted_kept(m4.mask, planted4, b4)}
-        del m4
+        log("mask from fp8 keys at 128K")
+        paths["sparse_prefill_n131072_b128"]["fp8_keys_mask"] = fp8_key_mask(q4, k4_bits, w4, 1 / math.sqrt(128), m4,
+                                                                              planted4, args.long_reps)
+        del m4, k4_bits
         log("query-aware rescue at 128K")
         paths["sparse_prefill_n131072_b128"]["query_aware_rescue"] = query_aware(
             q4, k4, v4, o4, w4, 1 / math.sqrt(128), t128, planted4, args.long_reps)

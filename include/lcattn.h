@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define LCATTN_ABI_VERSION 5
+#define LCATTN_ABI_VERSION 6
 
 typedef enum {
     ATTN_OK = 0,
@@ -120,6 +120,19 @@ size_t attn_block_mask_workspace_bytes(const attn_shape_t* shape, const attn_mas
 attn_status_t attn_block_mask_build(const attn_shape_t* shape, const attn_mask_params_t* params, const void* q,
                                     const void* k, uint8_t* mask, int32_t* kv_count, int32_t* kv_index,
                                     double* radius_stats, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_block_mask_build with the keys given as 8-bit E4M3 codes, one scale per tensor (key = code value * k_scale;
+ * OCP E4M3 as for attn_decode_paged_fp8). The centroids and radii are computed from those key values, which asks
+ * whether the rescue signal survives eight-bit keys ("Your 128K Context Is 6x Slower Than It Needs to Be", section
+ * "The numbers, stated honestly": the benchmark model's FP8 keys kept accuracy). Each code is widened exactly and
+ * scaled once in float64; every later step, output and the workspace are attn_block_mask_build's.
+ *   k_codes  E4M3 [batch, heads_kv, seq_len, head_dim] (16-byte aligned); q bf16 as before; k_scale finite > 0.
+ */
+attn_status_t attn_block_mask_build_fp8k(const attn_shape_t* shape, const attn_mask_params_t* params, const void* q,
+                                         const uint8_t* k_codes, float k_scale, uint8_t* mask, int32_t* kv_count,
+                                         int32_t* kv_index, double* radius_stats, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 /*
  * Block-sparse causal prefill: dense prefill restricted, for query row t of query block i = t / block_size, to

@@ -61,6 +61,7 @@ class AttnDecodeShape(ctypes.Structure):
 
 
 EXPORTS = ("attn_prefill_dense", "attn_block_mask_workspace_bytes", "attn_block_mask_build",
+           "attn_block_mask_build_fp8k",
            "attn_prefill_block_sparse", "attn_prefill_paged", "attn_prefill_paged_workspace_bytes",
            "attn_decode_workspace_bytes", "attn_decode_paged",
            "attn_decode_paged_fp8", "attn_status_string", "attn_last_error", "attn_abi_version")
@@ -97,6 +98,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_block_mask_build.restype = i32
     lib.attn_block_mask_build.argtypes = [ctypes.POINTER(AttnShape), ctypes.POINTER(AttnMaskParams), vp, vp, vp, vp,
                                           vp, vp, vp, sz, vp]
+    lib.attn_block_mask_build_fp8k.restype = i32
+    lib.attn_block_mask_build_fp8k.argtypes = [ctypes.POINTER(AttnShape), ctypes.POINTER(AttnMaskParams), vp, vp,
+                                               ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_prefill_block_sparse.restype = i32
     lib.attn_prefill_block_sparse.argtypes = [ctypes.POINTER(AttnShape), i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.attn_prefill_paged.restype = i32
@@ -211,12 +215,26 @@ def block_mask_workspace_bytes(q: torch.Tensor, k: torch.Tensor, block_size: int
 def block_mask_build(q: torch.Tensor, k: torch.Tensor, block_size: int, keep_permille: int, rescue_alpha: float,
                      q_lo_pct: int = 50, q_hi_pct: int = 90, scale: Optional[float] = None,
                      want_radius_stats: bool = True, workspace: Optional[torch.Tensor] = None,
-                     outputs: Optional[BlockMask] = None, stream=None, rescue_mode: int = 0) -> BlockMask:
-    """The centroid + radius-rescue block mask (bf16 q/k). Returns the mask, CSR lists and optional stats.
+                     outputs: Optional[BlockMask] = None, stream=None, rescue_mode: int = 0,
+                     k_scale: Optional[float] = None) -> BlockMask:
+    """The centroid + radius-rescue block mask. Returns the mask, CSR lists and optional stats.
     rescue_mode 0 rescues a flagged block in every row; 1 keeps it only in rows whose centroid cutoff its
-    score plus the radius allowance beats."""
+    score plus the radius allowance beats. q is bf16; k is bf16, or E4M3 codes (uint8) with k_scale."""
     lib = load()
-    shp = _prefill_shape(q, k, k, scale)
+    fp8k = k.dtype == torch.uint8
+    if fp8k and k_scale is None:
+        raise LcattnError(2, "fp8 key codes need k_scale")
+    if fp8k:
+        _need(q, "q", torch.bfloat16, 4)
+        _need(k, "k", torch.uint8, 4)
+        if k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
+            raise LcattnError(2, "k codes must be [B, Hkv, N, D] matching q")
+        _same_device(q.device, (k, "k"))
+        Dq = q.shape[3]
+        shp = AttnShape(q.shape[0], q.shape[1], k.shape[1], q.shape[2], Dq,
+                        1.0 / math.sqrt(Dq) if scale is None else float(scale), ATTN_BF16)
+    else:
+        shp = _prefill_shape(q, k, k, scale)
     prm = AttnMaskParams(block_size, keep_permille, float(rescue_alpha), q_lo_pct, q_hi_pct, rescue_mode)
     need = int(lib.attn_block_mask_workspace_bytes(ctypes.byref(shp), ctypes.byref(prm)))
     if need == 0:   # the library rejects these parameters; this call reports why
@@ -241,6 +259,12 @@ def block_mask_build(q: torch.Tensor, k: torch.Tensor, block_size: int, keep_per
         _like(outputs.radius_stats, "radius_stats", (B, Hkv, nb + 3), torch.float64, dev)
     _need(outputs.workspace, "workspace", torch.uint8)
     _same_device(dev, (outputs.workspace, "workspace"))
+    if fp8k:
+        _check(lib.attn_block_mask_build_fp8k(ctypes.byref(shp), ctypes.byref(prm), _ptr(q), _ptr(k), float(k_scale),
+                                              _ptr(outputs.mask), _ptr(outputs.kv_count), _ptr(outputs.kv_index),
+                                              _ptr(outputs.radius_stats), _ptr(outputs.workspace),
+                                              outputs.workspace.numel(), _stream(stream, dev)))
+        return outputs
     _check(lib.attn_block_mask_build(ctypes.byref(shp), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(outputs.mask),
                                      _ptr(outputs.kv_count), _ptr(outputs.kv_index), _ptr(outputs.radius_stats),
                                      _ptr(outputs.workspace), outputs.workspace.numel(), _stream(stream, dev)))

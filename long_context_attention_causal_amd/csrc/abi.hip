@@ -155,13 +155,16 @@ size_t attn_block_mask_workspace_bytes(const attn_shape_t* shape, const attn_mas
         .total;
 }
 
-attn_status_t attn_block_mask_build(const attn_shape_t* shape, const attn_mask_params_t* params, const void* q,
-                                    const void* k, uint8_t* mask, int32_t* kv_count, int32_t* kv_index,
-                                    double* radius_stats, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+attn_status_t mask_build(const attn_shape_t* shape, const attn_mask_params_t* params, const void* q, const void* k,
+                         const uint8_t* k8, double k_scale, uint8_t* mask, int32_t* kv_count, int32_t* kv_index,
+                         double* radius_stats, void* workspace, size_t workspace_bytes, void* stream,
+                         const char* what) {
     attn_status_t st = check_prefill_shape(shape, true);
     if (st != ATTN_OK) return st;
     if ((st = check_mask_params(shape, params)) != ATTN_OK) return st;
-    if ((st = check_ptrs({q, k, mask, kv_count, kv_index})) != ATTN_OK) return st;
+    if ((st = check_ptrs({q, k8 ? static_cast<const void*>(k8) : k, mask, kv_count, kv_index})) != ATTN_OK) return st;
     if (radius_stats && !aligned16(radius_stats)) return fail(ATTN_ERR_ALIGN, "radius_stats must be 16-byte aligned");
     const int nb = shape->seq_len / params->block_size;
     const lcattn::MaskWorkspace need = lcattn::mask_workspace_layout(shape->batch, shape->heads_q, shape->heads_kv,
@@ -175,6 +178,8 @@ attn_status_t attn_block_mask_build(const attn_shape_t* shape, const attn_mask_p
     lcattn::MaskProblem p;
     p.q = q;
     p.k = k;
+    p.k8 = k8;
+    p.k_scale = k_scale;
     p.B = shape->batch;
     p.Hq = shape->heads_q;
     p.Hkv = shape->heads_kv;
@@ -192,7 +197,26 @@ attn_status_t attn_block_mask_build(const attn_shape_t* shape, const attn_mask_p
     p.kv_count = kv_count;
     p.kv_index = kv_index;
     p.radius_stats = radius_stats;
-    return hip_status(lcattn::launch_block_mask(p, ws, static_cast<hipStream_t>(stream)), "attn_block_mask_build");
+    return hip_status(lcattn::launch_block_mask(p, ws, static_cast<hipStream_t>(stream)), what);
+}
+
+}  // namespace
+
+attn_status_t attn_block_mask_build(const attn_shape_t* shape, const attn_mask_params_t* params, const void* q,
+                                    const void* k, uint8_t* mask, int32_t* kv_count, int32_t* kv_index,
+                                    double* radius_stats, void* workspace, size_t workspace_bytes, void* stream) {
+    return mask_build(shape, params, q, k, nullptr, 1.0, mask, kv_count, kv_index, radius_stats, workspace,
+                      workspace_bytes, stream, "attn_block_mask_build");
+}
+
+attn_status_t attn_block_mask_build_fp8k(const attn_shape_t* shape, const attn_mask_params_t* params, const void* q,
+                                         const uint8_t* k_codes, float k_scale, uint8_t* mask, int32_t* kv_count,
+                                         int32_t* kv_index, double* radius_stats, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    if (!(std::isfinite(k_scale) && k_scale > 0.0f)) return fail(ATTN_ERR_SHAPE, "k_scale must be finite and > 0");
+    if (!k_codes) return fail(ATTN_ERR_NULL, "k_codes is NULL");
+    return mask_build(shape, params, q, nullptr, k_codes, (double)k_scale, mask, kv_count, kv_index, radius_stats,
+                      workspace, workspace_bytes, stream, "attn_block_mask_build_fp8k");
 }
 
 attn_status_t attn_prefill_block_sparse(const attn_shape_t* shape, int32_t block_size, const void* q,

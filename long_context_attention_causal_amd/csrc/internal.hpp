@@ -25,7 +25,9 @@ hipError_t launch_prefill_sparse_bf16(const PrefillProblem& p, int block, const 
 
 struct MaskProblem {
     const void* q;
-    const void* k;
+    const void* k;         // bf16 keys, unless k8 is set
+    const uint8_t* k8 = nullptr;   // E4M3 key codes, value = code value * k_scale
+    double k_scale = 1.0;
     int B, Hq, Hkv, N, D, block, nb;
     double scale;
     int keep_permille;

@@ -30,7 +30,9 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) { return (double)
 
 struct StatsArgs {
     const uint16_t* q;
-    const uint16_t* k;
+    const uint16_t* k;     // bf16 keys, or
+    const uint8_t* k8;     // E4M3 key codes (value = code value * k_scale) when set
+    double k_scale;
     double* qbar;
     double* kbar;
     double* radius;
@@ -38,7 +40,20 @@ struct StatsArgs {
     long nq_blocks;  // B * Hq * nb
 };
 
-template <int D>
+// Eight keys of a row from E4M3 codes, widened exactly (fp8 -> f32 is exact) and scaled in f64 (one rounding).
+__device__ __forceinline__ void fp8x8_to_f64(u32x2 w, double k_scale, double (&x)[8]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[h], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[h], true);
+        x[4 * h + 0] = (double)lo[0] * k_scale;
+        x[4 * h + 1] = (double)lo[1] * k_scale;
+        x[4 * h + 2] = (double)hi[0] * k_scale;
+        x[4 * h + 3] = (double)hi[1] * k_scale;
+    }
+}
+
+template <int D, bool K8>
 __global__ __launch_bounds__(256) void mask_stats_kernel(const StatsArgs a) {
     constexpr int CPR = D / 8;        // 16-byte chunks per row
     constexpr int RPP = 256 / CPR;    // rows per pass
@@ -49,6 +64,7 @@ __global__ __launch_bounds__(256) void mask_stats_kernel(const StatsArgs a) {
     long id = blockIdx.x;
     const bool isq = id < a.nq_blocks;
     const uint16_t* base;
+    const uint8_t* base8 = nullptr;
     double* out;
     int b, hh, j;
     if (isq) {
@@ -64,16 +80,29 @@ __global__ __launch_bounds__(256) void mask_stats_kernel(const StatsArgs a) {
         const long bg = id / a.nb;
         hh = (int)(bg % a.Hkv);
         b = (int)(bg / a.Hkv);
-        base = a.k + (((size_t)b * a.Hkv + hh) * a.N + (size_t)j * a.block) * D;
+        const size_t row0 = (((size_t)b * a.Hkv + hh) * a.N + (size_t)j * a.block) * D;
+        base = K8 ? nullptr : a.k + row0;
+        base8 = K8 ? a.k8 + row0 : nullptr;
         out = a.kbar + (((size_t)b * a.Hkv + hh) * a.nb + j) * D;
     }
+    // eight consecutive elements of row r (this lane's chunk), as f64
+    auto elems = [&](int r, double (&x)[8]) {
+        if (K8 && !isq) {
+            fp8x8_to_f64(*reinterpret_cast<const u32x2*>(base8 + (size_t)r * D + c * 8), a.k_scale, x);
+        } else {
+            const u32x4 v = load16(base + (size_t)r * D + c * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = bf16_to_f64((v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+        }
+    };
     double s[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] = 0.0;
     for (int r = r0; r < a.block; r += RPP) {
-        const u32x4 v = load16(base + (size_t)r * D + c * 8);
+        double x[8];
+        elems(r, x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] += bf16_to_f64((v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+        for (int e = 0; e < 8; ++e) s[e] += x[e];
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) part[r0][c * 8 + e] = s[e];
@@ -92,11 +121,12 @@ __global__ __launch_bounds__(256) void mask_stats_kernel(const StatsArgs a) {
     for (int e = 0; e < 8; ++e) cc[e] = cen[c * 8 + e];
     double best = 0.0;
     for (int r = r0; r < a.block; r += RPP) {
-        const u32x4 v = load16(base + (size_t)r * D + c * 8);
+        double xs[8];
+        elems(r, xs);
         double d2 = 0.0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const double x = bf16_to_f64((v[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu) - cc[e];
+            const double x = xs[e] - cc[e];
             d2 += x * x;
         }
 #pragma unroll
@@ -435,7 +465,9 @@ MaskWorkspace mask_workspace_layout(int B, int Hq, int Hkv, int nb, int D, char*
 hipError_t launch_block_mask(const MaskProblem& p, const MaskWorkspace& ws, hipStream_t s) {
     StatsArgs sa;
     sa.q = static_cast<const uint16_t*>(p.q);
-    sa.k = static_cast<const uint16_t*>(p.k);
+    sa.k = p.k8 ? nullptr : static_cast<const uint16_t*>(p.k);
+    sa.k8 = p.k8;
+    sa.k_scale = p.k_scale;
     sa.qbar = ws.qbar;
     sa.kbar = ws.kbar;
     sa.radius = ws.radius;
@@ -447,8 +479,13 @@ hipError_t launch_block_mask(const MaskProblem& p, const MaskWorkspace& ws, hipS
     sa.nb = p.nb;
     sa.nq_blocks = (long)p.B * p.Hq * p.nb;
     const unsigned nstat = (unsigned)(sa.nq_blocks + (long)p.B * p.Hkv * p.nb);
-    if (p.D == 128) hipLaunchKernelGGL((mask_stats_kernel<128>), dim3(nstat), dim3(256), 0, s, sa);
-    else hipLaunchKernelGGL((mask_stats_kernel<64>), dim3(nstat), dim3(256), 0, s, sa);
+    if (p.k8) {
+        if (p.D == 128) hipLaunchKernelGGL((mask_stats_kernel<128, true>), dim3(nstat), dim3(256), 0, s, sa);
+        else hipLaunchKernelGGL((mask_stats_kernel<64, true>), dim3(nstat), dim3(256), 0, s, sa);
+    } else {
+        if (p.D == 128) hipLaunchKernelGGL((mask_stats_kernel<128, false>), dim3(nstat), dim3(256), 0, s, sa);
+        else hipLaunchKernelGGL((mask_stats_kernel<64, false>), dim3(nstat), dim3(256), 0, s, sa);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 

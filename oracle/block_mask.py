@@ -193,3 +193,14 @@ def build_mask(q: np.ndarray, k: np.ndarray, scale: float, block: int, keep_perm
     return MaskResult(mask=mask, kv_count=kv_count, kv_index=kv_index, radius=rad, med=med, p90=p90, tau=tau,
                       rescue=rescue, centroid=cen, cut_gap=gap, score_absmax=amax, rescued=resc, lam=lam,
                       qnorm=qnorm, rescue_gap=rgap)
+
+
+def build_mask_fp8_keys(q: np.ndarray, k_codes: np.ndarray, k_scale: float, scale: float, block: int,
+                        keep_permille: int, alpha: float, lo_pct: int = 50, hi_pct: int = 90,
+                        rescue_mode: int = 0) -> MaskResult:
+    """build_mask with the keys given as 8-bit E4M3 codes and one scale per tensor: every key is its code's value
+    times k_scale, in float64, and the rule is then applied unchanged ("Your 128K Context Is 6x Slower Than It
+    Needs to Be", section "The numbers, stated honestly", reports the rescue signal holding with FP8 keys)."""
+    from oracle.attention import e4m3_value
+    k = e4m3_value(k_codes) * float(k_scale)
+    return build_mask(q, k, scale, block, keep_permille, alpha, lo_pct, hi_pct, rescue_mode)

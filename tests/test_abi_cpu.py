@@ -31,14 +31,14 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     decl = declared_functions()
-    assert len(decl) == 12
+    assert len(decl) == 13
     for name in decl:
         assert hasattr(L, name), name
     assert set(decl) == set(lca.EXPORTS)
 
 
 def test_version_and_status_strings(L):
-    assert lca.abi_version() == 5
+    assert lca.abi_version() == 6
     for st in range(7):
         assert L.attn_status_string(st)
     assert L.attn_status_string(99) == b"unknown status"
@@ -243,3 +243,14 @@ def test_prefill_paged_workspace_policy(L):
     windowed = pshape(B=8, Hq=64, Hkv=8, D=64, Nq=2048, maxp=1024, pages=8000, window=128)
     assert L.attn_prefill_paged_workspace_bytes(ctypes.byref(windowed)) == 0
     assert L.attn_prefill_paged_workspace_bytes(ctypes.byref(pshape(D=96))) == 0
+
+
+def test_mask_build_fp8k_checks(L):
+    s, p = shape(), params()
+    need = L.attn_block_mask_workspace_bytes(ctypes.byref(s), ctypes.byref(p))
+    call = lambda ks, k=FAKE, ws=need: L.attn_block_mask_build_fp8k(ctypes.byref(s), ctypes.byref(p), FAKE, k, ks,
+                                                                    FAKE, FAKE, FAKE, None, FAKE, ws, None)
+    assert call(0.0) == 2 and call(math.nan) == 2 and call(-1.0) == 2
+    assert call(1.0, k=None) == 1
+    assert call(1.0, k=MISALIGNED) == 4
+    assert call(1.0, ws=need - 1) == 5

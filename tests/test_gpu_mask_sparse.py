@@ -74,6 +74,53 @@ def compare_mask(lib, inp, keep, alpha, label, lo=50, hi=90, mode=0):
     return m, ref
 
 
+def compare_mask_fp8_keys(lib, inp, keep, alpha, label, lo=50, hi=90, mode=0):
+    """The mask from E4M3 key codes (per-tensor scale) against the oracle applied to the dequantised keys."""
+    codes, ksc = W.e4m3_keys(inp.k)
+    ksc32 = float(np.float32(ksc))
+    q, _, _ = prefill_to_device(inp)
+    say(f"[mask fp8k] {label} mode {mode}: gpu")
+    m = lib.block_mask_build(q, torch.from_numpy(codes).cuda(), inp.block, keep, alpha, lo, hi, scale=inp.scale,
+                             rescue_mode=mode, k_scale=ksc32)
+    torch.cuda.synchronize()
+    qf, _, _ = inp.as_f64()
+    ref = M.build_mask_fp8_keys(qf, codes, ksc32, float(np.float32(inp.scale)), inp.block, keep, alpha, lo, hi,
+                                rescue_mode=mode)
+    G = inp.q.shape[1] // inp.k.shape[1]
+    nb = ref.mask.shape[-1]
+    rs = m.radius_stats.cpu().numpy()
+    np.testing.assert_allclose(rs[..., :nb], ref.radius, rtol=1e-12, atol=0)
+    amb = ambiguous_rows(ref, G)
+    mask = m.mask.cpu().numpy()
+    bad = (mask != ref.mask).any(axis=-1)
+    say(f"[mask fp8k] {label} mode {mode}: rows={bad.size} mismatched={int(bad.sum())} ambiguous={int(amb.sum())}")
+    assert not (bad & ~amb).any(), "fp8-key mask differs outside the documented tie band"
+    return m, ref
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("B,Hq,Hkv,N,D,block,keep,alpha", [
+    (2, 8, 2, 64 * 40, 128, 64, 100, 1.0),
+    (1, 4, 4, 128 * 20, 64, 128, 50, 1.0),
+])
+def test_mask_fp8_keys_small(lib, B, Hq, Hkv, N, D, block, keep, alpha, mode):
+    inp = W.planted_inputs(46, B, Hq, Hkv, N, D, block)
+    compare_mask_fp8_keys(lib, inp, keep, alpha, f"small {B},{Hq},{Hkv},{N},{D},b{block}", mode=mode)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_mask_fp8_keys_c3(lib, mode):
+    """The 32K workload's mask from fp8 keys: bit-exact with the oracle, and every planted block still kept in the row
+    of its query (the rescue signal survives eight-bit keys on this workload)."""
+    w = W.WORKLOADS["c3_sparse_bf16_n32k"]
+    inp = W.planted_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["block"])
+    m, ref = compare_mask_fp8_keys(lib, inp, w["keep_permille"], w["alpha"], "c3", w["q_lo_pct"], w["q_hi_pct"],
+                                   mode)
+    mask = m.mask.cpu().numpy()
+    for (b, g, j, u, h, t) in inp.planted:
+        assert mask[b, h, t // w["block"], j] == 1
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,N,D,block,keep,alpha", [
     (2, 8, 2, 64 * 40, 128, 64, 100, 1.0),
     (1, 4, 4, 128 * 20, 64, 128, 50, 1.0),

@@ -354,3 +354,37 @@ def test_radius_quintile_diagnostic_synthetic_analogue():
     plain = _radius_quintile_share(W.dense_inputs(3, 1, 8, 2, 64 * 64, 64, "bf16"), 64)
     assert planted >= 0.9
     assert 0.1 <= plain <= 0.3
+
+
+# ------------------------------------------------------------------------------------------------- fp8 keys
+def test_fp8_key_mask_is_the_mask_of_the_dequantised_keys():
+    """Keys that are E4M3 values times a power of two: the fp8-key mask must equal build_mask on those exact keys
+    (scale applied once, to the key, not to the radius or the score)."""
+    from oracle import attention as A
+    rng = np.random.default_rng(80)
+    codes = rng.integers(0, 0x7F, size=(1, 2, 64 * 12, 16), dtype=np.uint8)   # finite, non-negative codes
+    codes[..., ::2] |= 0x80                                                    # and negative ones
+    kscale = 2.0 ** -5
+    k = A.e4m3_value(codes) * kscale
+    q = rnd(81, 1, 4, 64 * 12, 16)
+    for mode in (0, 1):
+        a = M.build_mask_fp8_keys(q, codes, kscale, 0.25, 64, 150, 1.0, rescue_mode=mode)
+        b = M.build_mask(q, k, 0.25, 64, 150, 1.0, rescue_mode=mode)
+        np.testing.assert_array_equal(a.mask, b.mask)
+        np.testing.assert_array_equal(a.radius, b.radius)
+    # a different scale moves the radii and the scores by the same factor: the quantile-based flags and the
+    # centroid ranking are scale-free, so the mask is unchanged while the radii scale
+    c = M.build_mask_fp8_keys(q, codes, 4 * kscale, 0.25, 64, 150, 1.0)
+    np.testing.assert_array_equal(c.mask, M.build_mask_fp8_keys(q, codes, kscale, 0.25, 64, 150, 1.0).mask)
+    np.testing.assert_allclose(c.radius, 4 * b.radius, rtol=1e-15)
+
+
+def test_e4m3_keys_calibration():
+    inp = W.planted_inputs(3, 1, 4, 2, 64 * 8, 32, 64)
+    codes, sc = W.e4m3_keys(inp.k)
+    from oracle import attention as A
+    k = W.f64_from_bf16_bits(inp.k)
+    kq = A.e4m3_value(codes) * sc
+    assert np.abs(A.e4m3_value(codes)).max() <= 448 and (codes & 0x7F).max() <= 0x7E
+    # E4M3 keeps 3 mantissa bits: within 2^-4 relative in the normal range, a subnormal quantum below it
+    assert np.all(np.abs(kq - k) <= np.abs(k) * 2.0 ** -4 + sc * 2.0 ** -10)

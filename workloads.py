@@ -72,6 +72,16 @@ def e4m3_codes_from_f32(x: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
+def e4m3_keys(k_bits: np.ndarray) -> Tuple[np.ndarray, float]:
+    """Per-tensor E4M3 codes of bf16 keys: the scale maps the largest |key| onto 448 (computed in fp32), and each
+    code is the E4M3 rounding of key / scale. Returns (codes uint8 like k_bits, scale)."""
+    k32 = f32_from_bf16_bits(k_bits)
+    scale = float(np.float32(np.abs(k32).max()) / np.float32(448.0))
+    if scale == 0.0:
+        scale = 1.0
+    return e4m3_codes_from_f32(k32 / np.float32(scale)), scale
+
+
 def streams(seed: int, names: List[str]) -> Dict[str, np.random.Generator]:
     """Independent PCG64 generators, one per purpose, spawned from one SeedSequence."""
     children = np.random.SeedSequence(seed).spawn(len(names))
