@@ -63,7 +63,8 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the 32K/128K dense and 128K sparse lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--long-reps", type=int, default=3)
-    ap.add_argument("--only", choices=["dense", "dense32k", "sparse", "decode", "decode8", "copy"], default=None,
+    ap.add_argument("--only", choices=["dense", "dense32k", "sparse", "decode", "decode8", "paged", "copy"],
+                    default=None,
                     help="run one path alone (for profiler runs); prints a short JSON line with its mean time")
     ap.add_argument("--selector-sweep", action="store_true",
                     help="selector footprint and block-size sweep (N 32K..256K, blocks 64/128/256, both rescue "
@@ -542,6 +543,16 @@ def run_only(args, lca, W, torch, np, to_dev, dev):
                                  scale=c.scale, outputs=m)
             lca.prefill_block_sparse(q, k, v, m.kv_count, m.kv_index, w["block"], scale=c.scale, out=o,
                                      return_lse=False)
+    elif args.only == "paged":
+        w = W.WORKLOADS["c6_paged_prefill_chunk"]
+        p = W.make("c6_paged_prefill_chunk")
+        q, kc, vc = to_dev(p.q), to_dev(p.cache.k_cache), to_dev(p.cache.v_cache)
+        bt, sl = torch.from_numpy(p.cache.block_table).to(dev), torch.from_numpy(p.cache.seq_lens).to(dev)
+        o = torch.empty_like(q)
+        wsb = lca.prefill_paged_workspace_bytes(q, kc, bt, window=w["window"])
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+        fn = lambda: lca.prefill_paged(q, kc, vc, bt, sl, window=w["window"], scale=p.scale, out=o, return_lse=False,
+                                       workspace=ws)
     elif args.only == "decode8":
         w = W.WORKLOADS["c5_decode_paged_fp8"]
         c = W.make("c5_decode_paged_fp8")

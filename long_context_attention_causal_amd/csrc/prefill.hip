@@ -645,11 +645,11 @@ void prefill_paged_kernel(const PagedArgs a) {
     const int qabs = q0abs + (lane & 31);
     const int hi_key = base + min(a.Nq, p0 + a.PPW) - 1;   // latest key any row of the work-group sees
     const int lo_key = a.window > 0 ? max(0, base + p0 - a.window + 1) : 0;
-    const int t_first = lo_key / kBN;
-    const int ntiles_all = hi_key >= 0 ? hi_key / kBN - t_first + 1 : 0;
+    // tiles start at the page holding the earliest key, so a window's span needs no tile more than it covers
+    const int k_first = lo_key / kPageTokens * kPageTokens;
+    const int ntiles_all = hi_key >= 0 ? (hi_key - k_first) / kBN + 1 : 0;
     // this work-group's share of the tiles: split blockIdx.y of gridDim.y
     const int per_split = (ntiles_all + a.splits - 1) / a.splits;
-    const int t0 = t_first + (int)blockIdx.y * per_split;
     const int ntiles = max(0, min(per_split, ntiles_all - (int)blockIdx.y * per_split));
 
     const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)a.Nq * D;
@@ -680,7 +680,7 @@ void prefill_paged_kernel(const PagedArgs a) {
         kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.kc + slab), (short)0, valid * D * 2, 0x00020000);
         vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.vc + slab), (short)0, valid * D * 2, 0x00020000);
     };
-    int kv = t0 * kBN;
+    int kv = k_first + (int)blockIdx.y * per_split * kBN;
     if (ntiles > 0) {
         __amdgpu_buffer_rsrc_t kr, vr;
         views(kv, kr, vr);
