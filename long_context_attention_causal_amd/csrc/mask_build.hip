@@ -218,18 +218,18 @@ struct ScoreArgs {
     double scale;
 };
 
-// 128 x 128 output tile per work-group (rows: the kv head's query heads stacked, hl * nb + i; columns: key blocks),
-// 8 x 8 per thread, the head dim in chunks of 8 through double-buffered LDS with the next chunk loaded into registers
-// while the current one is used. Thread (tr, tc) of a 16 x 16 grid owns rows 8 tr .. 8 tr + 7 and columns
-// 32 k + 2 tc + {0, 1}, k = 0..3 (so a 16-lane row of column reads is one contiguous 256-byte run). The head-dim sum
-// runs in order d = 0 .. D-1 with one fma per term, as before. Tiles wholly above the diagonal are skipped.
-constexpr int kST = 128;    // tile edge
-constexpr int kSC = 8;      // head-dim chunk
-constexpr int kSP = kST + 2; // LDS row stride in doubles (16-byte aligned rows)
-__global__ __launch_bounds__(256) void mask_scores_kernel(const ScoreArgs a) {
-    __shared__ __attribute__((aligned(16))) double As[2][kSC][kSP];
-    __shared__ __attribute__((aligned(16))) double Bs[2][kSC][kSP];
-    const int tid = threadIdx.x, tr = tid / 16, tc = tid % 16;
+// 128 x 128 output tile per work-group (rows: the kv head's query heads stacked, hl * nb + i; columns: key blocks) on
+// the fp64 matrix cores: each wave owns a 64 x 64 quarter as 4 x 4 blocks of v_mfma_f64_16x16x4f64, the head dim
+// in chunks of 16 staged through LDS, the next chunk loaded into registers while the current one is multiplied.
+// Tiles wholly above the diagonal are skipped.
+constexpr int kST = 128;      // tile edge
+constexpr int kSC = 16;       // head-dim chunk (doubles)
+constexpr int kSP = kSC + 1;  // LDS row stride in doubles
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mask_scores_kernel(const ScoreArgs a) {
+    __shared__ double As[kST * kSP];
+    __shared__ double Bs[kST * kSP];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int j0 = blockIdx.x * kST, r0 = blockIdx.y * kST;
     const int bg = blockIdx.z, b = bg / a.Hkv, g = bg % a.Hkv;
     const int R = a.G * a.nb;
@@ -237,77 +237,73 @@ __global__ __launch_bounds__(256) void mask_scores_kernel(const ScoreArgs a) {
     const int imax = (r0 / a.nb == rl / a.nb) ? rl % a.nb : a.nb - 1;
     if (j0 > imax) return;
     const double* kb = a.kbar + ((size_t)b * a.Hkv + g) * a.nb * a.D;
-    // loader: thread -> (row or key block lr = tid / 2, head-dim half lh = tid % 2: 4 doubles)
-    const int lr = tid / 2, lh = tid % 2;
+    // loader: thread -> (row or key block lr = tid / 2, half lh = tid % 2 of the chunk: 8 doubles)
+    const int lr = tid >> 1, lh = tid & 1;
     const int ra = r0 + lr, ja = j0 + lr;
     const double* qsrc = nullptr;
     if (ra < R) {
         const int hl = ra / a.nb, i = ra % a.nb;
-        qsrc = a.qbar + (((size_t)b * a.Hq + g * a.G + hl) * a.nb + i) * a.D + 4 * lh;
+        qsrc = a.qbar + (((size_t)b * a.Hq + g * a.G + hl) * a.nb + i) * a.D + 8 * lh;
     }
-    const double* ksrc = ja < a.nb ? kb + (size_t)ja * a.D + 4 * lh : nullptr;
-    auto fetch = [&](int d0, double (&qa)[4], double (&ka)[4]) {
+    const double* ksrc = ja < a.nb ? kb + (size_t)ja * a.D + 8 * lh : nullptr;
+    double qa[8], ka[8];
+    auto fetch = [&](int d0) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            qa[k] = qsrc ? qsrc[d0 + k] : 0.0;
-            ka[k] = ksrc ? ksrc[d0 + k] : 0.0;
+        for (int k = 0; k < 8; k += 2) {
+            const double2 x = qsrc ? *reinterpret_cast<const double2*>(qsrc + d0 + k) : double2{0.0, 0.0};
+            const double2 y = ksrc ? *reinterpret_cast<const double2*>(ksrc + d0 + k) : double2{0.0, 0.0};
+            qa[k] = x.x;
+            qa[k + 1] = x.y;
+            ka[k] = y.x;
+            ka[k + 1] = y.y;
         }
     };
-    auto stash = [&](int buf, const double (&qa)[4], const double (&ka)[4]) {
+    const int wr = (w >> 1) * 64, wc = (w & 1) * 64;   // the wave's quarter
+    const int fi = lane & 15, fk = lane >> 4;            // operand lane: row (column) fi, head dim fk of 4
+    f64x4 acc[4][4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            As[buf][4 * lh + k][lr] = qa[k];
-            Bs[buf][4 * lh + k][lr] = ka[k];
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[m][n] = f64x4{0.0, 0.0, 0.0, 0.0};
+    fetch(0);
+    for (int d0 = 0; d0 < a.D; d0 += kSC) {
+        __syncthreads();   // every wave is done with the previous chunk
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            As[lr * kSP + 8 * lh + k] = qa[k];
+            Bs[lr * kSP + 8 * lh + k] = ka[k];
         }
-    };
-    double acc[8][8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int v = 0; v < 8; ++v) acc[u][v] = 0.0;
-    double qa[4], ka[4];
-    fetch(0, qa, ka);
-    stash(0, qa, ka);
-    __syncthreads();
-    const int nch = a.D / kSC;
-    for (int ch = 0; ch < nch; ++ch) {
-        const int buf = ch & 1;
-        if (ch + 1 < nch) fetch((ch + 1) * kSC, qa, ka);
-#pragma unroll
-        for (int dd = 0; dd < kSC; ++dd) {
-            double x[8], y[8];
-#pragma unroll
-            for (int u = 0; u < 8; u += 2) {
-                const double2 t = *reinterpret_cast<const double2*>(&As[buf][dd][8 * tr + u]);
-                x[u] = t.x;
-                x[u + 1] = t.y;
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const double2 t = *reinterpret_cast<const double2*>(&Bs[buf][dd][32 * k + 2 * tc]);
-                y[2 * k] = t.x;
-                y[2 * k + 1] = t.y;
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-                for (int v = 0; v < 8; ++v) acc[u][v] = fma(x[u], y[v], acc[u][v]);
-        }
-        if (ch + 1 < nch) stash(buf ^ 1, qa, ka);
         __syncthreads();
-    }
+        if (d0 + kSC < a.D) fetch(d0 + kSC);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int r = r0 + 8 * tr + u;
-        if (r >= R) continue;
-        const int hl = r / a.nb, i = r % a.nb;
-        double* srow = a.scores + (((size_t)b * a.Hq + g * a.G + hl) * a.nb + i) * a.nb;
+        for (int ks = 0; ks < kSC / 4; ++ks) {
+            double av[4], bv[4];
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int j = j0 + 32 * (v / 2) + 2 * tc + (v % 2);
-            if (j <= i && j < a.nb) srow[j] = __dmul_rn(a.scale, acc[u][v]);
+            for (int m = 0; m < 4; ++m) av[m] = As[(wr + 16 * m + fi) * kSP + 4 * ks + fk];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) bv[n] = Bs[(wc + 16 * n + fi) * kSP + 4 * ks + fk];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int n = 0; n < 4; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[m], bv[n], acc[m][n], 0, 0, 0);
         }
     }
+    // block (m, n) element v of lane l is row 16 m + l / 16 + 4 v, column 16 n + l % 16 of the quarter
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = r0 + wr + 16 * m + fk + 4 * v;
+            if (r >= R) continue;
+            const int hl = r / a.nb, i = r % a.nb;
+            double* srow = a.scores + (((size_t)b * a.Hq + g * a.G + hl) * a.nb + i) * a.nb;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int j = j0 + wc + 16 * n + fi;
+                if (j <= i && j < a.nb) srow[j] = __dmul_rn(a.scale, acc[m][n][v]);
+            }
+        }
 }
 
 struct SelectArgs {
