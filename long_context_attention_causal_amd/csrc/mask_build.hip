@@ -339,12 +339,18 @@ __global__ __launch_bounds__(256) void mask_select_kernel(const SelectArgs a) {
     const uint8_t* fl = a.flags + ((size_t)b * a.Hkv + g) * a.nb;
     const int cand = i + 1;
     const int budget = min(cand, (int)(((long)cand * a.keep + 999) / 1000));
+    // slots e with 64 e > i hold no candidate in any lane: the counting loops skip them (a uniform branch).
+    // Every lane loads its scores and flags at a clamped index (always inside the row), so the loads issue
+    // back to back instead of one guarded load and wait per slot.
     uint64_t key[E];
     bool kept[E];
+    uint8_t fv[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int j = lane + 64 * e;
-        key[e] = j <= i ? order_key(srow[j]) : 0ull;
+        const double x = srow[min(j, i)];
+        fv[e] = fl[min(j, i)];
+        key[e] = order_key(x) & (0ull - (uint64_t)(j <= i));   // arithmetic, so the load stays unconditional
         kept[e] = false;
     }
     if (budget >= cand) {
@@ -357,7 +363,8 @@ __global__ __launch_bounds__(256) void mask_select_kernel(const SelectArgs a) {
             const uint64_t c = T | (1ull << bit);
             int cnt = 0;
 #pragma unroll
-            for (int e = 0; e < E; ++e) cnt += __popcll(__ballot((lane + 64 * e) <= i && key[e] >= c));
+            for (int e = 0; e < E; ++e)
+                if (64 * e <= i) cnt += __popcll(__ballot((lane + 64 * e) <= i && key[e] >= c));
             if (cnt >= budget) {
                 T = c;
                 if (cnt == budget) {
@@ -422,7 +429,7 @@ __global__ __launch_bounds__(256) void mask_select_kernel(const SelectArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int j = lane + 64 * e;
-        bool resc = j <= i && fl[j] != 0;
+        bool resc = j <= i && fv[e] != 0;
         if (aware && resc && !kept[e]) {
 #pragma clang fp contract(off)
             resc = srow[j] + coef * (rad[j] - med) > cut;
