@@ -221,7 +221,11 @@ struct ScoreArgs {
 // 128 x 128 output tile per work-group (rows: the kv head's query heads stacked, hl * nb + i; columns: key blocks) on
 // the fp64 matrix cores: each wave owns a 64 x 64 quarter as 4 x 4 blocks of v_mfma_f64_16x16x4f64, the head dim
 // in chunks of 16 staged through LDS, the next chunk loaded into registers while the current one is multiplied.
-// Tiles wholly above the diagonal are skipped.
+// Tiles wholly above the diagonal are skipped. The grid is one-dimensional over (kv group, row tile, column tile),
+// and work-group L takes tile (L % 8) * (total / 8) + L / 8 when the tile count divides by 8: the hardware deals
+// work-groups to the 8 XCDs round-robin, so each XCD then takes one contiguous eighth of the tiles, whose share of
+// the lower triangle is even (with column tiles innermost, XCD x would take every tile of column x, from all rows
+// for x = 0 down to the last row tile only for x = 7).
 constexpr int kST = 128;      // tile edge
 constexpr int kSC = 16;       // head-dim chunk (doubles)
 constexpr int kSP = kSC + 1;  // LDS row stride in doubles
@@ -230,9 +234,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     __shared__ double As[kST * kSP];
     __shared__ double Bs[kST * kSP];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int j0 = blockIdx.x * kST, r0 = blockIdx.y * kST;
-    const int bg = blockIdx.z, b = bg / a.Hkv, g = bg % a.Hkv;
     const int R = a.G * a.nb;
+    const int nct = (a.nb + kST - 1) / kST, nrt = (R + kST - 1) / kST;
+    const int total = (int)gridDim.x, L = (int)blockIdx.x;
+    const int T = total % 8 == 0 ? (L % 8) * (total / 8) + L / 8 : L;
+    const int j0 = (T % nct) * kST, r0 = ((T / nct) % nrt) * kST;
+    const int bg = T / (nct * nrt), b = bg / a.Hkv, g = bg % a.Hkv;
     const int rl = min(r0 + kST - 1, R - 1);
     const int imax = (r0 / a.nb == rl / a.nb) ? rl % a.nb : a.nb - 1;
     if (j0 > imax) return;
@@ -514,8 +521,9 @@ hipError_t launch_block_mask(const MaskProblem& p, const MaskWorkspace& ws, hipS
     sc.nb = p.nb;
     sc.D = p.D;
     sc.scale = p.scale;
-    const dim3 sgrid((unsigned)((p.nb + kST - 1) / kST), (unsigned)((sc.G * p.nb + kST - 1) / kST),
-                     (unsigned)(p.B * p.Hkv));
+    const long ntiles = (long)((p.nb + kST - 1) / kST) * ((sc.G * p.nb + kST - 1) / kST) * p.B * p.Hkv;
+    if (ntiles > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    const dim3 sgrid((unsigned)ntiles);
     hipLaunchKernelGGL(mask_scores_kernel, sgrid, dim3(256), 0, s, sc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
