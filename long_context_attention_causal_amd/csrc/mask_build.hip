@@ -159,6 +159,42 @@ __device__ double interp7(double xlo, double xhi, long num, bool has_next) {
     return xlo + f * (xhi - xlo);
 }
 
+// The four order statistics around the two quantile positions, by exact rank counting: work-group (bg, y) ranks
+// the 64 radii e = 64 y + lane against all n of its (batch, kv head), the four waves each counting a quarter of them.
+// The radius of sorted position k is the one x with #{y < x} <= k < #{y <= x} (equal radii write equal values), and
+// it lands in slot k of the (batch, kv head)'s four-double threshold record, which the threshold kernel then reads
+// and overwrites.
+__global__ __launch_bounds__(256) void mask_rank_kernel(const ThreshArgs a) {
+    __shared__ double rs[4096];
+    __shared__ int cnt[2][4][64];
+    const int bg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = a.nb;
+    const double* r = a.radius + (size_t)bg * n;
+    for (int e = tid; e < n; e += 256) rs[e] = r[e];
+    __syncthreads();
+    const int e = (int)blockIdx.y * 64 + lane;
+    const double x = rs[min(e, n - 1)];
+    const int q = (n + 3) / 4, t0 = w * q, t1 = min(n, t0 + q);
+    int lt = 0, le = 0;
+    for (int t = t0; t < t1; ++t) {
+        const double y = rs[t];
+        lt += (y < x);
+        le += (y <= x);
+    }
+    cnt[0][w][lane] = lt;
+    cnt[1][w][lane] = le;
+    __syncthreads();
+    if (w != 0 || e >= n) return;
+    lt = cnt[0][0][lane] + cnt[0][1][lane] + cnt[0][2][lane] + cnt[0][3][lane];
+    le = cnt[1][0][lane] + cnt[1][1][lane] + cnt[1][2][lane] + cnt[1][3][lane];
+    const long num_lo = (long)(n - 1) * a.lo_pct, num_hi = (long)(n - 1) * a.hi_pct;
+    const int want[4] = {(int)(num_lo / 100), (int)min((long)n - 1, num_lo / 100 + 1), (int)(num_hi / 100),
+                         (int)min((long)n - 1, num_hi / 100 + 1)};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (lt <= want[k] && want[k] < le) a.thresh[(size_t)bg * 4 + k] = x;
+}
+
+// One work-group per (batch, kv head): the quantiles from the ranked order statistics, tau and the flags.
 __global__ __launch_bounds__(1024) void mask_threshold_kernel(const ThreshArgs a) {
 #pragma clang fp contract(off)
     __shared__ double rs[4096];
@@ -166,23 +202,8 @@ __global__ __launch_bounds__(1024) void mask_threshold_kernel(const ThreshArgs a
     const int bg = blockIdx.x, tid = threadIdx.x, n = a.nb;
     const double* r = a.radius + (size_t)bg * n;
     for (int e = tid; e < n; e += 1024) rs[e] = r[e];
-    if (tid < 4) os[tid] = 0.0;
-    __syncthreads();
+    if (tid < 4) os[tid] = a.thresh[(size_t)bg * 4 + tid];
     const long num_lo = (long)(n - 1) * a.lo_pct, num_hi = (long)(n - 1) * a.hi_pct;
-    const int want[4] = {(int)(num_lo / 100), (int)min((long)n - 1, num_lo / 100 + 1), (int)(num_hi / 100),
-                         (int)min((long)n - 1, num_hi / 100 + 1)};
-    for (int e = tid; e < n; e += 1024) {
-        const double x = rs[e];
-        int lt = 0, le = 0;
-        for (int t = 0; t < n; ++t) {
-            const double y = rs[t];
-            lt += (y < x);
-            le += (y <= x);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (lt <= want[k] && want[k] < le) os[k] = x;  // every writer of a slot writes the same value
-    }
     __syncthreads();
     __shared__ double tau_s;
     if (tid == 0) {
@@ -508,6 +529,9 @@ hipError_t launch_block_mask(const MaskProblem& p, const MaskWorkspace& ws, hipS
     ta.lo_pct = p.lo_pct;
     ta.hi_pct = p.hi_pct;
     ta.alpha = p.alpha;
+    hipLaunchKernelGGL(mask_rank_kernel, dim3((unsigned)(p.B * p.Hkv), (unsigned)((p.nb + 63) / 64)), dim3(256), 0, s,
+                       ta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(mask_threshold_kernel, dim3((unsigned)(p.B * p.Hkv)), dim3(1024), 0, s, ta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
