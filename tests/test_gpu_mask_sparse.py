@@ -134,6 +134,17 @@ def test_mask_small(lib, B, Hq, Hkv, N, D, block, keep, alpha, mode):
     compare_mask(lib, inp, keep, alpha, f"small {B},{Hq},{Hkv},{N},{D},b{block},k{keep},a{alpha}", mode=mode)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("N", [131072, 262144])
+def test_mask_largest_block_counts(lib, N, mode):
+    """The select kernel's two widest instantiations: 2048 and 4096 (the library's maximum) key blocks per row,
+    64-row blocks, one kv head shared by two query heads."""
+    inp = W.planted_inputs(47, 1, 2, 1, N, 64, 64)
+    m, _ = compare_mask(lib, inp, 60, 1.0, f"largest nb={N // 64}", mode=mode)
+    del m
+    torch.cuda.empty_cache()
+
+
 def test_mask_special_rules(lib):
     inp = W.planted_inputs(42, 1, 8, 2, 64 * 30, 128, 64)
     nb = 30
