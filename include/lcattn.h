@@ -79,8 +79,10 @@ typedef struct {
  *   q, k, v  inputs in shape->dtype (bf16 or fp32), layouts as attn_shape_t.
  *   o        output, same dtype and layout as q.
  *   lse      optional fp32 [batch, heads_q, seq_len] (NULL to skip).
- * Supported: head_dim 64 or 128; bf16 (MFMA, fp32 accumulation) or fp32 (fp32 arithmetic throughout).
- * seq_len 0 is a no-op.
+ * Supported: head_dim 64 or 128; bf16 (MFMA, fp32 accumulation) or fp32 (fp32 arithmetic throughout);
+ * seq_len * head_dim * element size below 2^31 bytes (one head's K or V slab; 8,388,607 tokens at head_dim 128
+ * in bf16), else ATTN_ERR_UNSUPPORTED. The same bound holds for attn_block_mask_build(_fp8k) and
+ * attn_prefill_block_sparse. seq_len 0 is a no-op.
  */
 attn_status_t attn_prefill_dense(const attn_shape_t* shape, const void* q, const void* k, const void* v, void* o,
                                  float* lse, void* stream);

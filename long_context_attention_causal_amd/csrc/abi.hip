@@ -48,6 +48,11 @@ attn_status_t check_prefill_shape(const attn_shape_t* s, bool need_bf16) {
     if (need_bf16 && s->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "this operation supports bf16 only");
     const double elems = (double)s->batch * s->heads_q * s->seq_len * s->head_dim;
     if (elems > 9.0e15) return fail(ATTN_ERR_SHAPE, "tensor too large");
+    // the kernels address one head's K or V slab through a buffer view with a 32-bit signed byte extent
+    const long long slab = (long long)s->seq_len * s->head_dim * (s->dtype == ATTN_FP32 ? 4 : 2);
+    if (slab >= (1LL << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "seq_len %d x head_dim %d: a per-head K/V slab of %lld bytes exceeds 2^31 - 1",
+                    s->seq_len, s->head_dim, slab);
     if ((double)s->batch * s->heads_q * ((s->seq_len + 31) / 32) >= 4294967295.0)
         return fail(ATTN_ERR_SHAPE, "grid too large");
     return ATTN_OK;

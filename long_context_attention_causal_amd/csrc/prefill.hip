@@ -59,6 +59,8 @@ struct Lds {
     static_assert(KTILE % 1024 == 0 && VTILE % 1024 == 0, "tiles are filled by whole 1 KiB direct loads");
 };
 
+// One head's K or V slab. The host rejects shapes whose slab reaches 2^31 bytes, so `bytes` and every tile offset
+// kv0 * ROWB below stay within a signed 32-bit int.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, bytes, 0x00020000);
 }

@@ -67,6 +67,34 @@ def test_prefill_dense_rejects(L, s, code):
     assert L.attn_last_error()
 
 
+@pytest.mark.parametrize("N,D,dtype,code", [
+    (1 << 24, 128, 0, 3),          # 4 GiB per head: refused before any launch
+    ((1 << 23), 128, 0, 3),        # exactly 2^31 bytes
+    ((1 << 23) - 64, 128, 0, 1),   # accepted shape: the call then stops at the NULL q pointer
+    ((1 << 24) - 64, 64, 0, 1),
+    (1 << 24, 64, 0, 3),
+    ((1 << 22), 128, 1, 3),        # fp32: 4 bytes per element
+    ((1 << 22) - 64, 128, 1, 1),
+])
+def test_prefill_rejects_unaddressable_lengths(L, N, D, dtype, code):
+    """A per-head K/V slab of 2^31 bytes or more cannot be addressed by the kernels' 32-bit buffer views; such a
+    shape is refused with ATTN_ERR_UNSUPPORTED by every prefill-like entry point. An accepted shape is shown by the
+    next check failing instead (q is NULL), so no kernel is launched."""
+    s = shape(B=1, Hq=1, Hkv=1, N=N, D=D, dtype=dtype)
+    assert dense(L, s, q=None) == code
+    if code == 3:
+        assert b"2^31" in L.attn_last_error()
+    if dtype == 0 and code == 3:
+        # the shape check comes before the sparse path's own block-count limit
+        assert L.attn_prefill_block_sparse(ctypes.byref(s), 256, None, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                           None) == 3
+        assert b"2^31" in L.attn_last_error()
+    if dtype == 0:
+        p = params(block=2048)
+        ws = L.attn_block_mask_workspace_bytes(ctypes.byref(s), ctypes.byref(p))
+        assert (ws == 0) if code == 3 else (ws > 0 or N % 2048)
+
+
 def test_prefill_dense_pointer_checks(L):
     assert dense(L, shape(), q=None) == 1
     assert dense(L, shape(), v=MISALIGNED) == 4

@@ -9,6 +9,7 @@ import torch
 import workloads as W
 from oracle import attention as A
 from oracle import block_mask as M
+from tests import mask_check
 from tests.gpu_util import BF16_TOL, LSE_TOL, dev_i32, host64, max_err, prefill_to_device, say, take_rows
 
 pytestmark = pytest.mark.gpu
@@ -21,21 +22,23 @@ def gpu_mask(lib, inp, keep, alpha, lo=50, hi=90, mode=0):
     return m
 
 
-def ambiguous_rows(ref: M.MaskResult, G: int) -> np.ndarray:
-    """Rows whose result may legitimately differ between two correct fp64 evaluations: the centroid cut falls on
-    a score gap below 1e-12 relative, a radius lies within 1e-12 relative of its threshold, or (query-aware
-    rescue) a candidate's rescue score lies within 1e-12 relative of the row's cutoff."""
-    amb = (ref.cut_gap < 1e-12 * (1.0 + ref.score_absmax)) | (ref.rescue_gap < 1e-12)
-    tau = ref.tau[:, :, None]
-    near = np.isfinite(tau) & (np.abs(ref.radius - tau) <= 1e-12 * np.abs(tau))   # tau = inf flags nothing
-    B, Hq, nb = ref.kv_count.shape
-    for h in range(Hq):
-        touched = near[:, h // G, :]                      # [B, nb] key blocks
-        # a near-threshold key block j affects every row i >= j
-        first = np.where(touched.any(axis=1), touched.argmax(axis=1), nb)
-        for b in range(B):
-            amb[b, h, first[b]:] = True
-    return amb
+def check_against_oracle(m, ref, qf, kf, scale, keep, mode, label, tag="mask"):
+    """Every entry of the library's mask against the oracle's: entries fixed by the rule must match, entries in the
+    documented fp64 tie band may take either value within the row's pick count, and kv_count/kv_index must be the
+    CSR form of the library's own mask. The seeded workloads have no entry in the band, which is asserted."""
+    qbar, kbar, _ = M.block_stats(qf, kf, qf.shape[2] // ref.mask.shape[-1])
+    st = mask_check.entry_status(ref, qbar, kbar, scale, keep, mode)
+    mask = m.mask.cpu().numpy()
+    cnt = m.kv_count.cpu().numpy()
+    idx = m.kv_index.cpu().numpy()
+    nb = ref.mask.shape[-1]
+    diff = int((mask != ref.mask).sum())
+    say(f"[{tag}] {label} mode {mode}: rows={cnt.size} differing entries={diff} free entries="
+        f"{int(st.free.sum())} density={ref.mask.sum() / (cnt.size * (nb + 1) / 2):.4f}")
+    mask_check.check_mask(mask, cnt, idx, st, max_free=0)
+    # with no entry in the band the answer is unique
+    np.testing.assert_array_equal(mask, ref.mask)
+    np.testing.assert_array_equal(cnt, ref.kv_count)
 
 
 def compare_mask(lib, inp, keep, alpha, label, lo=50, hi=90, mode=0):
@@ -44,11 +47,8 @@ def compare_mask(lib, inp, keep, alpha, label, lo=50, hi=90, mode=0):
     q, k, _ = inp.as_f64()
     say(f"[mask] {label} mode {mode}: oracle")
     # the library takes the scale as float32
-    ref = M.build_mask(q, k, float(np.float32(inp.scale)), inp.block, keep, alpha, lo, hi, rescue_mode=mode)
-    G = inp.q.shape[1] // inp.k.shape[1]
-    mask = m.mask.cpu().numpy()
-    cnt = m.kv_count.cpu().numpy()
-    idx = m.kv_index.cpu().numpy()
+    sc = float(np.float32(inp.scale))
+    ref = M.build_mask(q, k, sc, inp.block, keep, alpha, lo, hi, rescue_mode=mode)
     rs = m.radius_stats.cpu().numpy()
     nb = ref.mask.shape[-1]
     # radii and thresholds: the same fp64 quantities up to summation order
@@ -57,20 +57,7 @@ def compare_mask(lib, inp, keep, alpha, label, lo=50, hi=90, mode=0):
         np.testing.assert_allclose(rs[..., nb + 2], ref.tau, rtol=1e-12, atol=0)
     np.testing.assert_allclose(rs[..., nb], ref.med, rtol=1e-12, atol=0)
     np.testing.assert_allclose(rs[..., nb + 1], ref.p90, rtol=1e-12, atol=0)
-    amb = ambiguous_rows(ref, G)
-    bad = (mask != ref.mask).any(axis=-1)
-    say(f"[mask] {label}: rows={bad.size} mismatched={int(bad.sum())} ambiguous={int(amb.sum())} "
-        f"density={ref.mask.sum() / (bad.size * (nb + 1) / 2):.4f}")
-    assert not (bad & ~amb).any(), "mask differs outside the documented tie band"
-    ok = ~amb
-    np.testing.assert_array_equal(cnt[ok], ref.kv_count[ok])
-    B, Hq = cnt.shape[:2]
-    for b in range(B):
-        for h in range(Hq):
-            for i in np.nonzero(ok[b, h])[0]:
-                c = cnt[b, h, i]
-                if not np.array_equal(idx[b, h, i, :c], ref.kv_index[b, h, i, :c]):
-                    raise AssertionError(f"kv_index differs at {(b, h, i)}")
+    check_against_oracle(m, ref, q, k, sc, keep, mode, label)
     return m, ref
 
 
@@ -83,18 +70,20 @@ def compare_mask_fp8_keys(lib, inp, keep, alpha, label, lo=50, hi=90, mode=0):
     m = lib.block_mask_build(q, torch.from_numpy(codes).cuda(), inp.block, keep, alpha, lo, hi, scale=inp.scale,
                              rescue_mode=mode, k_scale=ksc32)
     torch.cuda.synchronize()
+    del q
     qf, _, _ = inp.as_f64()
-    ref = M.build_mask_fp8_keys(qf, codes, ksc32, float(np.float32(inp.scale)), inp.block, keep, alpha, lo, hi,
-                                rescue_mode=mode)
-    G = inp.q.shape[1] // inp.k.shape[1]
+    sc = float(np.float32(inp.scale))
+    say(f"[mask fp8k] {label} mode {mode}: oracle")
+    ref = M.build_mask_fp8_keys(qf, codes, ksc32, sc, inp.block, keep, alpha, lo, hi, rescue_mode=mode)
     nb = ref.mask.shape[-1]
     rs = m.radius_stats.cpu().numpy()
     np.testing.assert_allclose(rs[..., :nb], ref.radius, rtol=1e-12, atol=0)
-    amb = ambiguous_rows(ref, G)
-    mask = m.mask.cpu().numpy()
-    bad = (mask != ref.mask).any(axis=-1)
-    say(f"[mask fp8k] {label} mode {mode}: rows={bad.size} mismatched={int(bad.sum())} ambiguous={int(amb.sum())}")
-    assert not (bad & ~amb).any(), "fp8-key mask differs outside the documented tie band"
+    np.testing.assert_allclose(rs[..., nb], ref.med, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(rs[..., nb + 1], ref.p90, rtol=1e-12, atol=0)
+    if not math.isinf(alpha):
+        np.testing.assert_allclose(rs[..., nb + 2], ref.tau, rtol=1e-12, atol=0)
+    kf = A.e4m3_value(codes) * ksc32
+    check_against_oracle(m, ref, qf, kf, sc, keep, mode, label, tag="mask fp8k")
     return m, ref
 
 
@@ -119,6 +108,53 @@ def test_mask_fp8_keys_c3(lib, mode):
     mask = m.mask.cpu().numpy()
     for (b, g, j, u, h, t) in inp.planted:
         assert mask[b, h, t // w["block"], j] == 1
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_mask_fp8_keys_c4(lib, mode):
+    """The 128K workload's mask from fp8 keys: bit-exact with the oracle (mask, kv_count, kv_index), and every
+    planted block still kept in the row of its query."""
+    w = W.WORKLOADS["c4_sparse_bf16_n128k"]
+    say("[mask fp8k] c4: generating inputs")
+    inp = W.planted_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["block"])
+    m, ref = compare_mask_fp8_keys(lib, inp, w["keep_permille"], w["alpha"], "c4", w["q_lo_pct"], w["q_hi_pct"],
+                                   mode)
+    mask = m.mask.cpu().numpy()
+    for (b, g, j, u, h, t) in inp.planted:
+        assert mask[b, h, t // w["block"], j] == 1
+    del m
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_mask_exact_ties_go_to_the_smaller_block(lib, mode):
+    """Every key block with the same centroid: each row's centroid scores tie exactly, on the GPU as in the oracle
+    (identical columns give identical fp64 products), and the rule's tie-break (the smaller block) decides. The radii
+    differ, so the rescue branch still flags blocks; the mask must be the oracle's bit for bit."""
+    B, Hq, Hkv, nb, blk, D = 1, 4, 2, 24, 64, 64
+    rng = np.random.default_rng(48)
+    q = rng.standard_normal((B, Hq, nb * blk, D)).astype(np.float32)
+    k = np.empty((B, Hkv, nb * blk, D), np.float32)
+    sign = np.where(np.arange(blk) % 2 == 0, 1.0, -1.0).astype(np.float32)[:, None]
+    for g in range(Hkv):
+        c = np.round(rng.standard_normal(D) * 4) / 4      # quarters: exact in bf16, exact block means
+        for j in range(nb):
+            d = np.round(rng.standard_normal(D) * 4 * (1 + j % 5)) / 4
+            k[0, g, j * blk:(j + 1) * blk] = c + sign * d
+    inp = W.PrefillInputs(q=W.bf16_bits_from_f32(q), k=W.bf16_bits_from_f32(k),
+                          v=W.bf16_bits_from_f32(np.zeros_like(k)), dtype="bf16", scale=1.0 / 8.0, block=blk)
+    assert np.array_equal(W.f64_from_bf16_bits(inp.k), k.astype(np.float64))
+    m = gpu_mask(lib, inp, 250, 1.0, mode=mode)
+    qf, kf, _ = inp.as_f64()
+    ref = M.build_mask(qf, kf, 0.125, blk, 250, 1.0, rescue_mode=mode)
+    say(f"[mask ties] mode {mode}: rows with a zero cut gap = {int((ref.cut_gap == 0).sum())}")
+    assert (ref.cut_gap == 0).sum() > 0
+    np.testing.assert_array_equal(m.mask.cpu().numpy(), ref.mask)
+    np.testing.assert_array_equal(m.kv_count.cpu().numpy(), ref.kv_count)
+    cnt = ref.kv_count
+    idx = m.kv_index.cpu().numpy()
+    for pos in np.ndindex(cnt.shape):
+        assert np.array_equal(idx[pos][:cnt[pos]], ref.kv_index[pos][:cnt[pos]])
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,N,D,block,keep,alpha", [
