@@ -2,17 +2,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-long] [--no-cpu-baseline]
 
-A step runs every variant once, each on its own synthetic workload, with inputs already resident in HBM:
-  dense   causal GQA prefill, B1 Hq32 Hkv4 D128 N4096 (the headline workload)
-  sparse  block-mask build + block-sparse prefill, N32768 block 64, centroid budget 10%, rescue alpha 1
+A step runs every step of the hot path once, each on its own synthetic workload, with inputs already resident in HBM:
+  dense   causal GQA prefill, B1 Hq32 Hkv4 D128 N32768, Q/K/V i.i.d. N(0,1) (the headline workload)
+  sparse  block-mask build + block-sparse prefill, N32768 block 64, planted outliers, centroid budget 10%, rescue
+          alpha 1
   decode  split-KV paged decode, B32 Hq64 Hkv8 D64, lengths U[1024, 32768], page 16, 512-token chunks
-`value` is the dense prefill's TFLOP/s (causal count 2*B*Hq*N^2*D over the kernel's own event-timed duration).
-After the timed steps the decode workload is also run over an fp8 (E4M3) copy of its cache, chunked prefill over a
-paged cache is timed (a 4K chunk closing a 32K sequence; a 128-token-window chunk over 8 sequences), and the
-long-context lines are measured on their own: dense prefill at 32K and 128K and the
-128K mask + sparse pass (speedup over the library's own dense kernel at the same length), and at 32K and 128K the mask
-built with the query-aware rescue (rescue_mode 1) and the sparse pass over it. The fp64 CPU oracle is timed
-on the host (cpu_baseline) on the headline workload. One JSON line goes to stdout.
+`value` is the dense prefill's TFLOP/s: the causal count 2*B*Hq*N^2*D over the kernel's own mean duration, taken with
+HIP events recorded around each call on the stream it is launched on. `ms_per_step` is the wall time of a whole step
+(all three paths); `headline_kernel_ms` is the dense call's mean event time alone.
+After the timed steps, further lines go under `paths`, each timed over at least 20 calls: dense prefill at N=4096 and
+at 128K; the decode workload timed cold and over an fp8 (E4M3) copy of its cache; chunked prefill over a paged
+cache (a 4K chunk closing a 32K sequence; a 128-token-window chunk over 8 sequences); the 128K mask + sparse pass
+(speedup over the library's own dense kernel at the same length); and at 32K and 128K the mask built with the
+query-aware rescue (rescue_mode 1) and from fp8 keys. The fp64 CPU oracle is timed on the host (cpu_baseline) on
+seeded sampled rows of the headline workload, with the full workload's time extrapolated from its rate. One JSON
+line goes to stdout.
 """
 from __future__ import annotations
 
@@ -62,7 +66,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-long", action="store_true", help="skip the 32K/128K dense and 128K sparse lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--long-reps", type=int, default=3)
+    ap.add_argument("--long-reps", type=int, default=20)
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="query rows per head the CPU oracle computes for cpu_baseline")
     ap.add_argument("--only", choices=["dense", "dense32k", "sparse", "decode", "decode8", "paged", "copy"],
                     default=None,
                     help="run one path alone (for profiler runs); prints a short JSON line with its mean time")
@@ -96,11 +102,11 @@ def main():
         return
 
     # ---------------------------------------------------------------------------------------- inputs
-    log("generating the headline dense workload (N=4096)")
-    w2 = W.WORKLOADS["c2_dense_bf16_n4k"]
-    c2 = W.make("c2_dense_bf16_n4k")
-    q2, k2, v2 = to_dev(c2.q), to_dev(c2.k), to_dev(c2.v)
-    o2 = torch.empty_like(q2)
+    log("generating the headline dense workload (N=32768, plain N(0,1))")
+    wh = W.WORKLOADS["dense_bf16_n32k"]
+    ch = W.make("dense_bf16_n32k")
+    qh, kh, vh = to_dev(ch.q), to_dev(ch.k), to_dev(ch.v)
+    oh = torch.empty_like(qh)
 
     log("generating the 32K block-sparse workload")
     w3 = W.WORKLOADS["c3_sparse_bf16_n32k"]
@@ -118,15 +124,15 @@ def main():
     sl5 = torch.from_numpy(c5.seq_lens).to(dev)
     maxlen5 = int(w5["len_hi"])
     o5 = torch.empty_like(q5)
-    ws5 = torch.empty(lca.decode_workspace_bytes(q5, kc5, bt5, maxlen5, w5["chunk"]), dtype=torch.uint8, device=dev)
+    ws5 = torch.zeros(lca.decode_workspace_bytes(q5, kc5, bt5, maxlen5, w5["chunk"]), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     def step(rec):
-        e = [ev() for _ in range(6)]
+        e = [ev() for _ in range(5)]
         e[0].record()
-        lca.prefill_dense(q2, k2, v2, scale=c2.scale, out=o2, return_lse=False)
+        lca.prefill_dense(qh, kh, vh, scale=ch.scale, out=oh, return_lse=False)
         e[1].record()
         lca.block_mask_build(q3, k3, w3["block"], w3["keep_permille"], w3["alpha"], w3["q_lo_pct"], w3["q_hi_pct"],
                              scale=c3.scale, outputs=m3)
@@ -151,12 +157,26 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = np.array([[r[i].elapsed_time(r[i + 1]) for i in range(4)] for r in recs])   # ms per part
-    t_dense, t_mask3, t_sparse3, t_dec = (float(x) for x in per.mean(axis=0))
+    t_head, t_mask3, t_sparse3, t_dec = (float(x) for x in per.mean(axis=0))
 
     def spread(x):   # median and the 10th / 90th percentiles of per-call times, ms
         x = np.asarray(x, dtype=np.float64)
         return {"ms_median": float(np.median(x)), "ms_p10": float(np.percentile(x, 10)),
-                "ms_p90": float(np.percentile(x, 90))}
+                "ms_p90": float(np.percentile(x, 90)), "calls": int(x.size)}
+
+    def time_calls(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        es = []
+        for _ in range(reps):
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            es.append((a, b))
+        torch.cuda.synchronize()
+        x = [a.elapsed_time(b) for a, b in es]
+        return float(np.mean(x)), spread(x)
 
     # decode timed cold as well: 1 GiB read between calls evicts L2 and the 256 MB last-level cache (a read rather than
     # a write, whose dirty lines would be written back during the decode and charge it for the eviction)
@@ -215,9 +235,9 @@ def main():
     del junk, q8, k8, v8, bt8, sl8, o8, c8
     torch.cuda.empty_cache()
 
-    B, Hq, N, D = c2.q.shape
-    fl2 = dense_flops(B, Hq, N, D)
-    tflops2 = fl2 / (t_dense * 1e-3) / 1e12
+    B, Hq, N, D = ch.q.shape
+    fl_head = dense_flops(B, Hq, N, D)
+    tf_head = fl_head / (t_head * 1e-3) / 1e12
 
     # sparse accounting from the mask the GPU built
     cnt3 = m3.kv_count.cpu().numpy().astype(np.int64)
@@ -239,15 +259,19 @@ def main():
     mask_read3 = float((w3["Hq"] + w3["Hkv"]) * w3["N"] * D3 * 2)
 
     paths = {
-        "dense_prefill_n4096": {"ms": t_dense, **spread(per[:, 0]), "tflops": tflops2,
-                                "pct_bf16_peak": 100 * tflops2 / PEAK_BF16_TFLOPS, "tokens_per_s": N / (t_dense * 1e-3)},
+        "dense_prefill_n32768": {"ms": t_head, **spread(per[:, 0]), "tflops": tf_head,
+                                 "pct_bf16_peak": 100 * tf_head / PEAK_BF16_TFLOPS,
+                                 "tokens_per_s": B * N / (t_head * 1e-3), "note": "the headline (value) line"},
         "mask_build_n32768_b64": {"ms": t_mask3, **spread(per[:, 1]), "stats_read_bytes": mask_read3,
                                   "stats_read_gbs_over_whole_build": mask_read3 / (t_mask3 * 1e-3) / 1e9,
                                   "density": density3},
         "sparse_prefill_n32768_b64": {"ms": t_sparse3, **spread(per[:, 2]), "executed_tflop": exec3 / 1e12,
                                       "executed_tflops": exec3 / (t_sparse3 * 1e-3) / 1e12,
                                       "pct_bf16_peak_executed": 100 * exec3 / (t_sparse3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                                      "dense_equiv_tflops_incl_mask": dense_eq3 / ((t_sparse3 + t_mask3) * 1e-3) / 1e12},
+                                      "dense_equiv_tflops_incl_mask": dense_eq3 / ((t_sparse3 + t_mask3) * 1e-3) / 1e12,
+                                      "speedup_vs_dense_kernel_only": t_head / t_sparse3,
+                                      "speedup_vs_dense_incl_mask": t_head / (t_sparse3 + t_mask3),
+                                      "planted_kept": None},
         "decode_paged_c5": {"ms": t_dec, **spread(per[:, 3]), "algorithmic_bytes": dec_bytes, "gbs": dec_gbs,
                             "cold_ms": float(np.mean(cold_ms)), "cold_ms_median": float(np.median(cold_ms)),
                             "cold_gbs": dec_bytes / (float(np.mean(cold_ms)) * 1e-3) / 1e9,
@@ -269,20 +293,6 @@ def main():
         "speedup_vs_bf16_cold": float(np.mean(cold_ms)) / float(np.mean(cold8_ms)),
         "measured_hbm_bytes": (lambda a, b: None if a is None or b is None else a + b)(
             measured_traffic("decode_split_fp8_c5", "decode.hip"), measured_traffic("decode_combine_fp8_c5", "decode.hip"))}
-
-    def time_calls(fn, reps):
-        fn()
-        torch.cuda.synchronize()
-        es = []
-        for _ in range(reps):
-            a, b = ev(), ev()
-            a.record()
-            fn()
-            b.record()
-            es.append((a, b))
-        torch.cuda.synchronize()
-        x = [a.elapsed_time(b) for a, b in es]
-        return float(np.mean(x)), spread(x)
 
     def planted_kept(mask, planted, block):
         """How many planted key blocks the mask keeps in the row of the query they were planted for."""
@@ -332,6 +342,20 @@ def main():
         return {"ms": t, **sp, "key_range_split": wsb > 0, "tflops": fl / (t * 1e-3) / 1e12, "pct_bf16_peak": 100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                 "new_tokens_per_s": w["B"] * Nq / (t * 1e-3), "flop": fl}
 
+    # dense prefill at N=4096 (the shorter dense workload)
+    log("dense prefill at N=4096")
+    c2 = W.make("c2_dense_bf16_n4k")
+    q2, k2, v2 = to_dev(c2.q), to_dev(c2.k), to_dev(c2.v)
+    o2 = torch.empty_like(q2)
+    t2, s2 = time_calls(lambda: lca.prefill_dense(q2, k2, v2, scale=c2.scale, out=o2, return_lse=False),
+                        max(args.long_reps, 20))
+    B2, Hq2, N2, D2 = c2.q.shape
+    tf2 = dense_flops(B2, Hq2, N2, D2) / (t2 * 1e-3) / 1e12
+    paths["dense_prefill_n4096"] = {"ms": t2, **s2, "tflops": tf2, "pct_bf16_peak": 100 * tf2 / PEAK_BF16_TFLOPS,
+                                    "tokens_per_s": N2 / (t2 * 1e-3),
+                                    "measured_hbm_bytes": measured_traffic("prefill_dense_c2", "prefill.hip")}
+    del q2, k2, v2, o2, c2
+
     paths["paged_prefill_c6_chunk4k_of_32k"] = paged_line("c6_paged_prefill_chunk", 20)
     paths["paged_prefill_c7_window128"] = paged_line("c7_paged_prefill_window", 20)
 
@@ -354,20 +378,13 @@ def main():
                 "jaccard_vs_bf16_keys": inter / union, "planted_kept": planted_kept(m.mask, planted, blk)}
 
     if not args.no_long:
-        log("dense prefill at 32K")
-        t32, s32 = time_calls(lambda: lca.prefill_dense(q3, k3, v3, scale=c3.scale, out=o3, return_lse=False),
-                              max(args.long_reps, 5))
-        tf32 = dense_eq3 / (t32 * 1e-3) / 1e12
-        paths["dense_prefill_n32768"] = {"ms": t32, **s32, "tflops": tf32, "pct_bf16_peak": 100 * tf32 / PEAK_BF16_TFLOPS}
-        paths["sparse_prefill_n32768_b64"]["speedup_vs_dense_kernel_only"] = t32 / t_sparse3
-        paths["sparse_prefill_n32768_b64"]["speedup_vs_dense_incl_mask"] = t32 / (t_sparse3 + t_mask3)
         paths["sparse_prefill_n32768_b64"]["planted_kept"] = planted_kept(m3.mask, c3.planted, w3["block"])
         log("query-aware rescue at 32K")
         paths["sparse_prefill_n32768_b64"]["query_aware_rescue"] = query_aware(
-            q3, k3, v3, o3, w3, c3.scale, t32, c3.planted, max(args.long_reps, 5))
+            q3, k3, v3, o3, w3, c3.scale, t_head, c3.planted, args.long_reps)
         log("mask from fp8 keys at 32K")
         paths["mask_build_n32768_b64"]["fp8_keys"] = fp8_key_mask(q3, c3.k, w3, c3.scale, m3, c3.planted,
-                                                                  max(args.long_reps, 5))
+                                                                  args.long_reps)
         del q3, k3, v3, o3, m3
         torch.cuda.empty_cache()
         log("generating the 128K block-sparse workload")
@@ -419,28 +436,50 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import attention as A
-        log("timing the fp64 oracle on the host (headline workload, all rows)")
-        qf, kf, vf = c2.as_f64()
+        rows = W.sample_rows(wh["seed"], N, Hq, args.cpu_rows)
+        log(f"timing the fp64 oracle on the host ({rows.shape[1]} seeded rows per head of the headline workload)")
         cores = len(os.sched_getaffinity(0))
-        t0 = time.perf_counter()
-        A.causal_attention(qf, kf, vf, c2.scale)
-        tc = time.perf_counter() - t0
-        cpu = {"value": fl2 / tc / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-               "sample": f"full dense causal GQA prefill B1 Hq32 Hkv4 D128 N4096 in float64 numpy, {tc:.2f} s "
-                         f"(BLAS threads = {os.environ.get('OMP_NUM_THREADS', 'default')})"}
+        G = Hq // ch.k.shape[1]
+        t_cpu = 0.0
+        sample_flop = 0.0
+        for h in range(Hq):
+            g = h // G
+            # widening the inputs to fp64 is preparation, not timed; the oracle's attention over the rows is
+            kf = W.f64_from_bf16_bits(ch.k[:, g:g + 1])
+            vf = W.f64_from_bf16_bits(ch.v[:, g:g + 1])
+            qf = np.zeros((B, 1, N, D))
+            qf[:, 0, rows[h]] = W.f64_from_bf16_bits(ch.q[:, h, rows[h]])
+            t0 = time.perf_counter()
+            A.causal_attention(qf, kf, vf, ch.scale, rows=rows[h])
+            t_cpu += time.perf_counter() - t0
+            sample_flop += 4.0 * D * float((rows[h] + 1).sum()) * B   # causal: row t sees t + 1 keys
+        rate = sample_flop / t_cpu
+        blas = "unknown"
+        try:
+            blas = str(np.show_config(mode="dicts")["Build Dependencies"]["blas"].get("name", "unknown"))
+        except Exception:
+            pass
+        cpu = {"value": rate / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": f"fp64 numpy oracle ({blas} BLAS, {os.environ.get('OMP_NUM_THREADS', 'default')} BLAS "
+                         f"threads) on {rows.size} seeded query rows ({rows.shape[1]} per head, all {Hq} heads, "
+                         f"rows 0 and N-1 included) of the headline workload: {sample_flop / 1e9:.1f} GFLOP of "
+                         f"causal work in {t_cpu:.2f} s; the full workload extrapolated at that rate",
+               "rows": int(rows.size), "seconds": t_cpu, "gflops": rate / 1e9,
+               "extrapolated_full_s": fl_head / rate, "blas": blas}
 
     line = {
-        "metric": METRIC, "value": tflops2, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "c2_dense_bf16_n4k: dense causal GQA prefill B1 Hq32 Hkv4 D128 N4096 "
-                               "(step also runs the N32768 mask+sparse pass and the paged decode)",
+        "metric": METRIC, "value": tf_head, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "headline_kernel_ms": t_head,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "dense_bf16_n32k: dense causal GQA prefill B1 Hq32 Hkv4 D128 N32768, Q/K/V i.i.d. "
+                               "N(0,1) in bf16 (value); a step also runs the N32768 block-64 mask build and "
+                               "block-sparse prefill and the paged decode (B32 Hq64 Hkv8 D64)",
                    "global_batch": 1, "seq_len": N, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "achieved": tflops2, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops2 / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic("prefill_dense_c2", "prefill.hip"),
-                     "kernel": "prefill_dense_kernel<128>", "per_launch_flop": fl2,
-                     "algorithmic_bytes": float((B * Hq + 2 * c2.k.shape[1]) * N * D * 2 + B * Hq * N * D * 2)},
+        "roofline": {"bound": "mfma", "achieved": tf_head, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf_head / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic("prefill_dense_n32k", "prefill.hip"),
+                     "kernel": "prefill_dense_kernel<128>", "per_launch_flop": fl_head,
+                     "algorithmic_bytes": float((B * Hq + 2 * ch.k.shape[1]) * N * D * 2 + B * Hq * N * D * 2)},
         "cpu_baseline": cpu,
         "paths": paths,
     }
@@ -525,7 +564,7 @@ def run_only(args, lca, W, torch, np, to_dev, dev):
         dst = torch.empty_like(src)
         fn = lambda: dst.copy_(src)
     elif args.only in ("dense", "dense32k"):
-        name = "c2_dense_bf16_n4k" if args.only == "dense" else "c3_sparse_bf16_n32k"
+        name = "c2_dense_bf16_n4k" if args.only == "dense" else "dense_bf16_n32k"
         c = W.make(name)
         q, k, v = to_dev(c.q), to_dev(c.k), to_dev(c.v)
         o = torch.empty_like(q)

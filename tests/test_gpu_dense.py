@@ -101,14 +101,20 @@ def test_row_zero_is_v0_and_uniform_v(lib):
     assert (o2.float() - ref).abs().max().item() <= 8e-3
 
 
-@pytest.mark.parametrize("name,per_head", [("c3_sparse_bf16_n32k", 256), ("c4_sparse_bf16_n128k", 256)])
+@pytest.mark.parametrize("name,per_head", [("dense_bf16_n32k", 256), ("c3_sparse_bf16_n32k", 256),
+                                           ("c4_sparse_bf16_n128k", 256)])
 def test_dense_long_sampled(lib, name, per_head):
-    """Dense prefill over the long-context workloads' Q/K/V (planted keys included), checked on 256 seeded
-    rows per head, always holding rows 0 and N-1, block-boundary rows and the planted query rows."""
+    """Dense prefill over the long-context workloads' Q/K/V, checked on 256 seeded rows per head, always holding
+    rows 0 and N-1 and block-boundary rows: the plain N(0,1) 32K workload the throughput line times (same inputs,
+    same launch), and the planted 32K/128K workloads, whose samples also hold every planted query row."""
     w = W.WORKLOADS[name]
     say(f"[dense] {name}: generating inputs")
-    inp = W.planted_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["block"])
-    rows = W.sample_rows(w["seed"], w["N"], w["Hq"], per_head, block=w["block"], planted=inp.planted)
+    if w["kind"] == "dense":
+        inp = W.make(name)
+        rows = W.sample_rows(w["seed"], w["N"], w["Hq"], per_head)
+    else:
+        inp = W.planted_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["D"], w["block"])
+        rows = W.sample_rows(w["seed"], w["N"], w["Hq"], per_head, block=w["block"], planted=inp.planted)
     q, k, v = prefill_to_device(inp)
     say(f"[dense] {name}: launching")
     o, lse = lib.prefill_dense(q, k, v, scale=inp.scale)

@@ -387,6 +387,9 @@ def sample_rows(seed: int, N: int, Hq: int, per_head: int, block: Optional[int] 
 WORKLOADS = {
     "c1_dense_fp32_n256": dict(kind="dense", seed=1, B=1, Hq=1, Hkv=1, N=256, D=64, dtype="fp32"),
     "c2_dense_bf16_n4k": dict(kind="dense", seed=2, B=1, Hq=32, Hkv=4, N=4096, D=128, dtype="bf16"),
+    # dense causal GQA prefill at 32K on plain N(0,1) inputs: the rescue page's model shape at the shorter of the
+    # two context lengths it compares
+    "dense_bf16_n32k": dict(kind="dense", seed=32, B=1, Hq=32, Hkv=4, N=32768, D=128, dtype="bf16"),
     "c3_sparse_bf16_n32k": dict(kind="sparse", seed=3, B=1, Hq=32, Hkv=4, N=32768, D=128, block=64,
                                 keep_permille=100, alpha=1.0, q_lo_pct=50, q_hi_pct=90),
     "c4_sparse_bf16_n128k": dict(kind="sparse", seed=4, B=1, Hq=32, Hkv=4, N=131072, D=128, block=128,
