@@ -109,3 +109,38 @@ def test_deterministic(lib):
     o1, l1 = run(lib, d)
     o2, l2 = run(lib, d)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_workspace_reuse_across_lengths(lib, fp8):
+    """One workspace reused across calls whose sequences change length (single-chunk, empty and many-chunk
+    sequences): the partials a call leaves behind never leak into the next call's result."""
+    B, Hq, Hkv, D, chunk, maxlen = 6, 16, 2, 64, 256, 3000
+    dev = torch.device("cuda", 0)
+    shape_q = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
+    shape_k = torch.empty(1, Hkv, 16, D, dtype=torch.bfloat16, device=dev)
+    bt0 = torch.empty(B, -(-maxlen // 16), dtype=torch.int32, device=dev)
+    ws = torch.empty(lib.decode_workspace_bytes(shape_q, shape_k, bt0, maxlen, chunk), dtype=torch.uint8, device=dev)
+    for trial, lens in enumerate([[3000, 1, 256, 0, 257, 2999], [100, 3000, 0, 0, 1500, 255],
+                                  [0, 0, 0, 0, 0, 0], [2048, 2048, 2048, 2048, 2048, 2048]]):
+        seed = 60 + trial
+        if fp8:
+            d = W.decode_inputs_fp8(seed, B, Hq, Hkv, D, 16, 1, maxlen, 2.0 ** -6, 2.0 ** -6, seq_lens=np.array(lens))
+            q, kc, vc = dev_bf16(d.q), torch.from_numpy(d.k_cache).cuda(), torch.from_numpy(d.v_cache_t).cuda()
+            bt, sl = dev_i32(d.block_table), dev_i32(d.seq_lens)
+            o, lse = lib.decode_paged_fp8(q, kc, vc, d.k_scale, d.v_scale, bt, sl, maxlen, chunk_tokens=chunk,
+                                          scale=d.scale, workspace=ws)
+            Oref, Lref = A.paged_decode_fp8(W.f64_from_bf16_bits(d.q), d.k_cache, d.v_cache_t, d.k_scale, d.v_scale,
+                                            d.block_table, d.seq_lens, d.scale)
+        else:
+            d = W.decode_inputs(seed, B, Hq, Hkv, D, 16, 1, maxlen, seq_lens=np.array(lens))
+            q, kc, vc, bt, sl = to_dev(d)
+            o, lse = lib.decode_paged(q, kc, vc, bt, sl, maxlen, chunk_tokens=chunk, scale=d.scale, workspace=ws)
+            Oref, Lref = oracle(d)
+        torch.cuda.synchronize()
+        og, lg = host64(o), host64(lse)
+        live = d.seq_lens > 0
+        say(f"[decode reuse] fp8={fp8} lens={lens} max|dO|={max_err(og, Oref):.3e}")
+        assert max_err(og, Oref) <= BF16_TOL
+        assert max_err(lg[live], Lref[live]) <= LSE_TOL
+        assert (og[~live] == 0).all() and np.isneginf(lg[~live]).all()
