@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define LCATTN_ABI_VERSION 6
+#define LCATTN_ABI_VERSION 7
 
 typedef enum {
     ATTN_OK = 0,
@@ -227,6 +227,23 @@ attn_status_t attn_decode_paged_fp8(const attn_decode_shape_t* shape, const void
                                     const uint8_t* v_cache_t, float k_scale, float v_scale,
                                     const int32_t* block_table, const int32_t* seq_lens, int32_t max_seq_len,
                                     void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged without a workspace argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops that must not call hipMalloc, harnesses that forbid allocation. The chunk partials go
+ * to a scratch array the library holds in each GPU's memory (LCATTN_DECODE_SCRATCH_BYTES per GPU, reserved when
+ * the library's device code is loaded on that GPU and held until the process ends); the call itself allocates
+ * nothing. Arguments, layouts, trusted inputs, outputs and results are attn_decode_paged's (the same kernels).
+ * A shape whose attn_decode_workspace_bytes(shape, max_seq_len) exceeds LCATTN_DECODE_SCRATCH_BYTES returns
+ * ATTN_ERR_WORKSPACE before anything is enqueued. Every call on one GPU uses that GPU's one scratch array: calls
+ * that overlap in time on the same GPU (different streams, or host threads, without ordering) race and may return
+ * wrong results; calls ordered on one stream are safe. Nothing in the scratch needs to start at zero: each call
+ * writes every partial it reads.
+ */
+#define LCATTN_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+attn_status_t attn_decode_paged_noalloc(const attn_decode_shape_t* shape, const void* q, const void* k_cache,
+                                        const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                                        int32_t max_seq_len, void* o, float* lse, void* stream);
 
 const char* attn_status_string(attn_status_t status);
 const char* attn_last_error(void);

@@ -64,7 +64,9 @@ EXPORTS = ("attn_prefill_dense", "attn_block_mask_workspace_bytes", "attn_block_
            "attn_block_mask_build_fp8k",
            "attn_prefill_block_sparse", "attn_prefill_paged", "attn_prefill_paged_workspace_bytes",
            "attn_decode_workspace_bytes", "attn_decode_paged",
-           "attn_decode_paged_fp8", "attn_status_string", "attn_last_error", "attn_abi_version")
+           "attn_decode_paged_fp8", "attn_decode_paged_noalloc", "attn_status_string", "attn_last_error",
+           "attn_abi_version")
+DECODE_SCRATCH_BYTES = 64 << 20   # LCATTN_DECODE_SCRATCH_BYTES
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -112,6 +114,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(AttnDecodeShape), i32]
     lib.attn_decode_paged.restype = i32
     lib.attn_decode_paged.argtypes = [ctypes.POINTER(AttnDecodeShape), vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.attn_decode_paged_noalloc.restype = i32
+    lib.attn_decode_paged_noalloc.argtypes = [ctypes.POINTER(AttnDecodeShape), vp, vp, vp, vp, vp, i32, vp, vp, vp]
     lib.attn_decode_paged_fp8.restype = i32
     lib.attn_decode_paged_fp8.argtypes = [ctypes.POINTER(AttnDecodeShape), vp, vp, vp, ctypes.c_float,
                                           ctypes.c_float, vp, vp, i32, vp, vp, vp, sz, vp]
@@ -339,6 +343,35 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                                  _ptr(seq_lens), int(max_seq_len), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
                                  _stream(stream, q.device)))
     return o, lse
+
+
+def decode_paged_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens: torch.Tensor, max_seq_len: int, chunk_tokens: int = 512,
+                         scale: Optional[float] = None, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         stream=None) -> None:
+    """decode_paged through the entry point that allocates nothing: the chunk partials live in the library's own
+    per-GPU scratch. `out` (and `lse`, when wanted) must be given; nothing is allocated here either."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if k_cache.shape != v_cache.shape:
+        raise LcattnError(2, "k_cache and v_cache shapes differ")
+    if block_table.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
+        raise LcattnError(2, "block_table and seq_lens need one row per sequence of q")
+    if out is None:
+        raise LcattnError(1, "out must be given (this entry point allocates nothing)")
+    _like(out, "out", q.shape, torch.bfloat16, q.device)
+    if lse is not None:
+        _like(lse, "lse", q.shape[:2], torch.float32, q.device)
+    _same_device(q.device, (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens"))
+    shp = _decode_shape(q, k_cache, block_table, chunk_tokens, scale)
+    _check(lib.attn_decode_paged_noalloc(ctypes.byref(shp), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                         _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(lse),
+                                         _stream(stream, q.device)))
 
 
 def decode_paged_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache_t: torch.Tensor, k_scale: float,

@@ -8,6 +8,8 @@
 #include "../../include/lcattn.h"
 #include "internal.hpp"
 
+static_assert(LCATTN_DECODE_SCRATCH_BYTES == lcattn::kDecodeScratchBytes, "header and library scratch sizes differ");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -380,6 +382,28 @@ attn_status_t attn_decode_paged_fp8(const attn_decode_shape_t* shape, const void
     if (st != ATTN_OK) return st;
     return hip_status(lcattn::launch_decode_paged_fp8(p, k_scale, v_scale, workspace, static_cast<hipStream_t>(stream)),
                       "attn_decode_paged_fp8");
+}
+
+attn_status_t attn_decode_paged_noalloc(const attn_decode_shape_t* shape, const void* q, const void* k_cache,
+                                        const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                                        int32_t max_seq_len, void* o, float* lse, void* stream) {
+    attn_status_t st = check_decode_shape(shape, max_seq_len);
+    if (st != ATTN_OK) return st;
+    const size_t need = lcattn::decode_workspace_bytes(shape->batch, shape->heads_q, shape->head_dim,
+                                                       shape->chunk_tokens, max_seq_len);
+    if (need > lcattn::kDecodeScratchBytes)
+        return fail(ATTN_ERR_WORKSPACE, "this shape needs %zu bytes of decode scratch; the library holds %zu per GPU",
+                    need, lcattn::kDecodeScratchBytes);
+    // validate everything else against a stand-in workspace before touching the device
+    lcattn::DecodeProblem p;
+    if ((st = decode_problem(shape, q, k_cache, v_cache, block_table, seq_lens, max_seq_len, o, lse,
+                             reinterpret_cast<void*>(uintptr_t(256)), lcattn::kDecodeScratchBytes, p)) != ATTN_OK)
+        return st;
+    void* scratch = nullptr;
+    if ((st = hip_status(lcattn::decode_scratch(&scratch), "attn_decode_paged_noalloc: scratch lookup")) != ATTN_OK)
+        return st;
+    return hip_status(lcattn::launch_decode_paged(p, scratch, static_cast<hipStream_t>(stream)),
+                      "attn_decode_paged_noalloc");
 }
 
 }  // extern "C"

@@ -15,6 +15,9 @@
 // so slots past it read as zeros and NaN padding cannot leak.
 // The wave partials are merged in LDS; the chunk's normalised output and natural-log lse go to the workspace.
 // Combine kernel: one wave per (sequence, query head) merges the chunks by log-sum-exp.
+#include <mutex>
+#include <vector>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -664,6 +667,30 @@ hipError_t launch_decode_paged(const DecodeProblem& p, void* workspace, hipStrea
         if (e != hipSuccess) return e;
     }
     return launch_combine(p, a.opart, a.lpart, a.C, s);
+}
+
+// Chunk partials of attn_decode_paged_noalloc: a file-scope device array, one copy per GPU, held until the process
+// ends. Host code never uses the array's name as an address (on the host it is only a stand-in for the symbol): the
+// device address is looked up once per device with hipGetSymbolAddress and cached.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+    static std::mutex mu;
+    static std::vector<void*> per_device;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)per_device.size() <= dev) per_device.resize(dev + 1, nullptr);
+    if (!per_device[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    return hipSuccess;
 }
 
 }  // namespace lcattn

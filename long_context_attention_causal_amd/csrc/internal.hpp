@@ -84,6 +84,10 @@ int paged_prefill_splits(int B, int Hq, int Hkv, int D, int Nq, int max_seq_len,
 size_t paged_prefill_workspace_bytes(int B, int Hq, int D, int Nq, int splits);
 
 size_t decode_workspace_bytes(int B, int Hq, int D, int chunk, int max_seq_len);
+// The library's own decode scratch (attn_decode_paged_noalloc): kDecodeScratchBytes per GPU, device address of the
+// current device's copy.
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_decode_paged(const DecodeProblem& p, void* workspace, hipStream_t s);
 // k_cache holds E4M3 codes [pages, Hkv, 16, D], v_cache E4M3 codes transposed per page [pages, Hkv, D, 16]
 hipError_t launch_decode_paged_fp8(const DecodeProblem& p, float k_scale, float v_scale, void* workspace,

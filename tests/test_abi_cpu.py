@@ -31,14 +31,14 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     decl = declared_functions()
-    assert len(decl) == 13
+    assert len(decl) == 14
     for name in decl:
         assert hasattr(L, name), name
     assert set(decl) == set(lca.EXPORTS)
 
 
 def test_version_and_status_strings(L):
-    assert lca.abi_version() == 6
+    assert lca.abi_version() == 7
     for st in range(7):
         assert L.attn_status_string(st)
     assert L.attn_status_string(99) == b"unknown status"
@@ -282,3 +282,25 @@ def test_mask_build_fp8k_checks(L):
     assert call(1.0, k=None) == 1
     assert call(1.0, k=MISALIGNED) == 4
     assert call(1.0, ws=need - 1) == 5
+
+
+def test_decode_noalloc_rejects_before_touching_the_device(L):
+    """The entry point without a workspace validates like attn_decode_paged, and refuses shapes whose partials
+    exceed the library's fixed per-GPU scratch, all on the host (no GPU here, so any device call would fail)."""
+    assert lca.DECODE_SCRATCH_BYTES == 64 << 20
+    noalloc = lambda s, maxlen, q=FAKE, o=FAKE: L.attn_decode_paged_noalloc(
+        ctypes.byref(s) if s is not None else None, q, FAKE, FAKE, FAKE, FAKE, maxlen, o, None, None)
+    assert noalloc(None, 1000) == 1
+    assert noalloc(dshape(page=8), 1000) == 3
+    assert noalloc(dshape(), 1000, q=None) == 1
+    assert noalloc(dshape(), 1000, o=MISALIGNED) == 4
+    # B=32, Hq=64, D=64, 512-token chunks, lengths up to 32768: 32 * 64 * 64 chunks * 64 * 4 B = 32 MiB fits
+    big = dshape(B=32, Hq=64, Hkv=8, D=64, maxp=2048, pages=100)
+    need = L.attn_decode_workspace_bytes(ctypes.byref(big), 32768)
+    assert 0 < need <= lca.DECODE_SCRATCH_BYTES
+    assert noalloc(big, 32768, q=None) == 1      # the shape is accepted; the NULL q is what stops it
+    # twice the length needs more than the scratch holds
+    bigger = dshape(B=32, Hq=64, Hkv=8, D=64, maxp=8192, pages=100)
+    assert L.attn_decode_workspace_bytes(ctypes.byref(bigger), 131072) > lca.DECODE_SCRATCH_BYTES
+    assert noalloc(bigger, 131072) == 5
+    assert b"scratch" in L.attn_last_error()
