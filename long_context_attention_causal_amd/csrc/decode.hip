@@ -350,10 +350,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const CombineArgs a
 
 // ------------------------------------------------------------------------------------------------- fp8 cache
 // The same split over an E4M3 cache: K pages token-major [16 x D] bytes, V pages transposed [D x 16] bytes, one
-// scale per cache. A lane's MFMA operands come straight from HBM: 8 bytes of a key row for the S^T product and 4
-// consecutive tokens of one head-dim row of V^T for the O^T product, each widened to bf16 by the hardware
-// conversion (exact: every E4M3 value is a bf16 number), so no LDS is needed until the merge. k_scale is folded
-// into the exponent scale and v_scale into the final normalisation.
+// scale per cache. Every load moves 16 bytes per lane. A lane reads 16 consecutive bytes of its token's key row per
+// 64 head dims; the head dims of the S^T product's contraction are taken in that order (the query operand uses the
+// same order, so the sum is unchanged). The transposed value pages go to LDS whole (one 1 KiB direct load per 64
+// head dims) and come back as the 4 consecutive tokens of one head-dim row that the A operand of the O^T product
+// holds per lane. Codes are widened to bf16 by the hardware conversion (exact: every E4M3 value is a bf16 number).
+// k_scale is folded into the exponent scale and v_scale into the final normalisation.
 struct SplitArgs8 {
     const uint16_t* q;
     const uint8_t* kc;
@@ -375,14 +377,19 @@ __device__ __forceinline__ uint32_t widen2(uint32_t w) {
 
 template <int D, int PB>
 struct Batch8 {
-    u32x2 k[PB][D / 32];     // 8 key bytes per 32-wide slice of the head dim
-    uint32_t v[PB][D / 16];  // 4 token bytes per 16-row tile of the head dim
+    u32x4 k[PB][D / 64];     // 16 key bytes per 64 head dims
     int tok0;
 };
 
 template <int D, int NW, int PB>
 __global__ __launch_bounds__(NW * 64) void decode_split_fp8_kernel(const SplitArgs8 a) {
     constexpr int KS = D / 32, DT = D / 16;
+    constexpr int KL = D / 64;                    // 16-byte key loads per lane and page
+    constexpr int VPAGE = kPage * D;              // bytes of one transposed value page
+    constexpr int VL = VPAGE / 1024;              // 1 KiB direct loads per value page
+    // the two V buffers are distinct arrays, so reads of one are known not to alias loads into the other
+    __shared__ __attribute__((aligned(1024))) char vbuf0[NW][PB * VPAGE];
+    __shared__ __attribute__((aligned(1024))) char vbuf1[NW][PB * VPAGE];
     __shared__ float red_o[NW * 16 * D];
     __shared__ float red_m[NW][16], red_l[NW][16];
     const int g = (int)(blockIdx.x % a.Hkv), c = (int)(blockIdx.x / a.Hkv), b = blockIdx.y;
@@ -394,20 +401,22 @@ __global__ __launch_bounds__(NW * 64) void decode_split_fp8_kernel(const SplitAr
     const int32_t* btrow = a.bt + (size_t)b * a.max_pages;
     const int my_page = wpage0 + lane;
     const int my_pid = (lane < a.ppw && my_page < a.max_pages) ? btrow[my_page] : 0;
+    // query operand in the key loads' head-dim order: k-slot i of lane group grp in step ks is head dim
+    // 64 * (ks / 2) + 16 * grp + 8 * (ks % 2) + i
     bf16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = n < a.G ? __builtin_bit_cast(bf16x8, load16(a.q + ((size_t)b * a.Hq + g * a.G + n) * D + 32 * ks +
-                                                                 8 * grp))
+        qf[ks] = n < a.G ? __builtin_bit_cast(bf16x8, load16(a.q + ((size_t)b * a.Hq + g * a.G + n) * D +
+                                                                 64 * (ks >> 1) + 16 * grp + 8 * (ks & 1)))
                          : bf16x8{};
     if (c * a.chunk >= L) return;  // uniform over the work-group
 
     const int npages_seq = (L + kPage - 1) / kPage;
     const int nbatch = ((a.ppw + 2 * PB - 1) / (2 * PB)) * 2;
-    constexpr int kLoads = (KS + DT) * PB;   // vector loads per batch
+    constexpr int kLoads = (KL + VL) * PB;   // vector loads per batch
     static_assert(kLoads < 64, "vmcnt holds at most 63");
 
-    auto issue = [&](int bi, Batch8<D, PB>& bt) {
+    auto issue = [&](int bi, int buf, Batch8<D, PB>& bt) {
         bt.tok0 = (wpage0 + bi * PB) * kPage;
 #pragma unroll
         for (int p = 0; p < PB; ++p) {
@@ -422,21 +431,21 @@ __global__ __launch_bounds__(NW * 64) void decode_split_fp8_kernel(const SplitAr
             const uint8_t* kbase = a.kc + ((size_t)pid * a.Hkv + g) * (size_t)(kPage * D);
             const uint8_t* vbase = a.vc + ((size_t)pid * a.Hkv + g) * (size_t)(kPage * D);
             // key rows past the sequence end read as zeros; the value page is read whole (its tokens are the
-            // inner dimension) and its bytes past the end are cleared below
+            // inner dimension) and its bytes past the end are cleared after the LDS read
             const __amdgpu_buffer_rsrc_t kr =
                 __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kbase), (short)0, valid * D, 0x00020000);
             const __amdgpu_buffer_rsrc_t vr =
-                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vbase), (short)0, valid ? kPage * D : 0,
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vbase), (short)0, valid ? VPAGE : 0,
                                                   0x00020000);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                bt.k[p][ks] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                            kr, n * D + 32 * ks + 8 * grp, 0, 0));
-            const int nv = min(max(valid - 4 * grp, 0), 4);   // this lane's tokens 4*grp .. 4*grp+3 that exist
-            const uint32_t keep = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
+            for (int h = 0; h < KL; ++h)
+                bt.k[p][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           kr, n * D + 64 * h + 16 * grp, 0, 0));
+            lds_char* dst = (buf ? (lds_char*)&vbuf1[w][0] : (lds_char*)&vbuf0[w][0]) + p * VPAGE;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                bt.v[p][dt] = __builtin_amdgcn_raw_buffer_load_b32(vr, (16 * dt + n) * kPage + 4 * grp, 0, 0) & keep;
+            for (int i = 0; i < VL; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(dst + i * 1024),
+                                                         16, (i * 64 + lane) * 16, 0, 0, 0);
         }
     };
 
@@ -448,8 +457,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_fp8_kernel(const SplitAr
     ones[0] = (__bf16)1.0f;
     ones[1] = (__bf16)1.0f;
 
-    auto run = [&](int bi, Batch8<D, PB>& cur, Batch8<D, PB>& nxt) {
-        issue(bi + 1, nxt);
+    auto run = [&](int bi, int buf, Batch8<D, PB>& cur, Batch8<D, PB>& nxt) {
+        issue(bi + 1, buf ^ 1, nxt);
         __builtin_amdgcn_s_waitcnt(0x0F70 | (kLoads & 15) | ((kLoads >> 4) << 14));
         f32x4 s[PB];
         float mx = -INFINITY;
@@ -458,8 +467,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_fp8_kernel(const SplitAr
             s[p] = f32x4{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 kw = {widen2<false>(cur.k[p][ks][0]), widen2<true>(cur.k[p][ks][0]),
-                                  widen2<false>(cur.k[p][ks][1]), widen2<true>(cur.k[p][ks][1])};
+                const uint32_t w0 = cur.k[p][ks >> 1][2 * (ks & 1)], w1 = cur.k[p][ks >> 1][2 * (ks & 1) + 1];
+                const u32x4 kw = {widen2<false>(w0), widen2<true>(w0), widen2<false>(w1), widen2<true>(w1)};
                 s[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qf[ks], s[p], 0, 0, 0);
             }
             const int tok = cur.tok0 + p * kPage + 4 * grp;
@@ -481,6 +490,10 @@ __global__ __launch_bounds__(NW * 64) void decode_split_fp8_kernel(const SplitAr
             m = mxs;
         }
         const float bias = (m == -INFINITY) ? 0.0f : -m;
+        // the value pages of this batch must be visible to every lane of the wave before the LDS reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int p = 0; p < PB; ++p) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[p][0], a.c2, bias));
@@ -491,20 +504,32 @@ __global__ __launch_bounds__(NW * 64) void decode_split_fp8_kernel(const SplitAr
             const bf16x4 pb = __builtin_bit_cast(bf16x4, (u32x2{w0, w1}));
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, l, false);
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, l, false);
-            // V^T[d = 16*dt + n][tokens 4*grp .. 4*grp+3] is the A operand of the 16x16x16 product as loaded
+            // this lane's tokens 4*grp .. 4*grp+3 that exist; bytes past the sequence end are cleared
+            const int valid = min(kPage, L - (cur.tok0 + p * kPage));
+            const int nv = min(max(valid - 4 * grp, 0), 4);
+            const uint32_t keep = nv >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nv)) - 1u);
+            const lds_char* vp = (buf ? (const lds_char*)&vbuf1[w][0] : (const lds_char*)&vbuf0[w][0]) + p * VPAGE;
+            // V^T[d = 16*dt + n][tokens 4*grp .. 4*grp+3] is the A operand of the 16x16x16 product as read
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const u32x2 vw = {widen2<false>(cur.v[p][dt]), widen2<true>(cur.v[p][dt])};
+                const uint32_t vw4 =
+                    *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(vp + (16 * dt + n) * kPage +
+                                                                                         4 * grp) & keep;
+                const u32x2 vw = {widen2<false>(vw4), widen2<true>(vw4)};
                 o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vw), pb, o[dt], 0, 0, 0);
             }
         }
+        // all lanes are done reading this buffer before the next batch's loads may target it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
     Batch8<D, PB> ba, bb;
-    issue(0, ba);
+    issue(0, 0, ba);
     for (int bi = 0; bi < nbatch; bi += 2) {
-        run(bi, ba, bb);
-        run(bi + 1, bb, ba);
+        run(bi, 0, ba, bb);
+        run(bi + 1, 1, bb, ba);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // the empty batch issued last
     l += __shfl_xor(l, 16);
@@ -613,11 +638,11 @@ hipError_t launch_decode_paged_fp8(const DecodeProblem& p, float k_scale, float 
     a.num_pages = p.num_pages;
     a.C = C ? C : 1;
     a.chunk = p.chunk;
-    // one wave per work-group while a wave's pages fit its 64 block-table lanes: with half the bytes per page a
-    // wave streams its whole share of the chunk (one wave of 32 pages measured 4% faster than two of 16 on the
-    // paged workload; 8 pages per batch was slower than 4)
+    // two waves per work-group up to 128 pages per chunk, four beyond (a wave holds at most 64 pages' block-table
+    // entries); on the paged workload (512-token chunks) two waves of 16 pages measured 4.6% faster than one of 32
+    // and 2.7% faster than four of 8, and 4 pages per batch beat 8
     const int pages = p.chunk / kPage;
-    const int nw = pages <= 64 ? 1 : pages <= 128 ? 2 : 4;
+    const int nw = pages <= 128 ? 2 : 4;
     const int pb = p.D == 64 ? 4 : 2;
     a.ppw = p.chunk / kPage / nw;
     a.c2 = p.scale * kLog2e * k_scale;
