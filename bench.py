@@ -69,7 +69,8 @@ def main():
     ap.add_argument("--long-reps", type=int, default=20)
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="query rows per head the CPU oracle computes for cpu_baseline")
-    ap.add_argument("--only", choices=["dense", "dense32k", "sparse", "decode", "decode8", "paged", "copy"],
+    ap.add_argument("--only", choices=["dense", "dense32k", "sparse", "sparse128k", "decode", "decode8", "paged",
+                                       "copy"],
                     default=None,
                     help="run one path alone (for profiler runs); prints a short JSON line with its mean time")
     ap.add_argument("--selector-sweep", action="store_true",
@@ -569,9 +570,10 @@ def run_only(args, lca, W, torch, np, to_dev, dev):
         q, k, v = to_dev(c.q), to_dev(c.k), to_dev(c.v)
         o = torch.empty_like(q)
         fn = lambda: lca.prefill_dense(q, k, v, scale=c.scale, out=o, return_lse=False)
-    elif args.only == "sparse":
-        w = W.WORKLOADS["c3_sparse_bf16_n32k"]
-        c = W.make("c3_sparse_bf16_n32k")
+    elif args.only in ("sparse", "sparse128k"):
+        name = "c3_sparse_bf16_n32k" if args.only == "sparse" else "c4_sparse_bf16_n128k"
+        w = W.WORKLOADS[name]
+        c = W.make(name)
         q, k, v = to_dev(c.q), to_dev(c.k), to_dev(c.v)
         o = torch.empty_like(q)
         m = lca.block_mask_build(q, k, w["block"], w["keep_permille"], w["alpha"], w["q_lo_pct"], w["q_hi_pct"],
