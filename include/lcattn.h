@@ -42,7 +42,11 @@ typedef enum {
     ATTN_ERR_UNSUPPORTED = 3,  /* valid request the library does not implement (dtype, head_dim ...) */
     ATTN_ERR_ALIGN = 4,        /* a base pointer is not 16-byte aligned                             */
     ATTN_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the *_workspace_bytes query        */
-    ATTN_ERR_HIP = 6           /* the HIP runtime reported an error while enqueueing                */
+    ATTN_ERR_HIP = 6,          /* the HIP runtime reported an error while enqueueing                */
+    /* Not statuses: these pin the enumeration's range to that of a 32-bit int, so any int32 value a caller
+     * passes (e.g. to attn_status_string) is a value of the type on the C++ side of the ABI. */
+    ATTN_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    ATTN_STATUS_RANGE_MAX_ = 2147483647
 } attn_status_t;
 
 typedef enum { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype_t;

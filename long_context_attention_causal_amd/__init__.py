@@ -21,7 +21,8 @@ from typing import Optional, Tuple
 import torch  # imported before the library so both bind the same HIP runtime (shared SONAME)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblcattn.so")
+# the in-tree build, unless LCATTN_LIB names another build of the same library (e.g. a sanitizer build)
+LIB_PATH = os.environ.get("LCATTN_LIB") or os.path.join(_HERE, "liblcattn.so")
 
 ATTN_BF16, ATTN_FP32 = 0, 1
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",

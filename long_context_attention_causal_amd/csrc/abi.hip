@@ -138,6 +138,7 @@ const char* attn_status_string(attn_status_t st) {
         case ATTN_ERR_ALIGN: return "misaligned pointer";
         case ATTN_ERR_WORKSPACE: return "workspace too small";
         case ATTN_ERR_HIP: return "HIP runtime error";
+        default: break;
     }
     return "unknown status";
 }
