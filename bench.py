@@ -340,8 +340,22 @@ def main():
         pos = (Lp[:, None] - Nq) + np.arange(Nq)[None, :]
         keys = np.minimum(pos + 1, w["window"]) if w["window"] > 0 else pos + 1
         fl = 4.0 * w["D"] * w["Hq"] * float(keys.sum())
-        return {"ms": t, **sp, "key_range_split": wsb > 0, "tflops": fl / (t * 1e-3) / 1e12, "pct_bf16_peak": 100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                "new_tokens_per_s": w["B"] * Nq / (t * 1e-3), "flop": fl}
+        # algorithmic bytes: the chunk's q read and o written, and every cached K/V row some query of the chunk sees
+        lo = np.maximum(pos[:, 0] - w["window"] + 1, 0) if w["window"] > 0 else np.zeros_like(Lp)
+        kv_rows = float((Lp - lo).sum())
+        nbytes = 2.0 * w["B"] * w["Hq"] * Nq * w["D"] * 2 + kv_rows * w["Hkv"] * w["D"] * 2 * 2
+        ai = fl / nbytes
+        line = {"ms": t, **sp, "key_range_split": wsb > 0, "tflops": fl / (t * 1e-3) / 1e12,
+                "pct_bf16_peak": 100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "new_tokens_per_s": w["B"] * Nq / (t * 1e-3), "flop": fl, "algorithmic_bytes": nbytes,
+                "flop_per_byte": ai, "gbs": nbytes / (t * 1e-3) / 1e9}
+        # below the ridge (about 315 flop/B) the bound is HBM: report the fraction of that roofline too
+        if ai < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+            line["bound"] = "hbm"
+            line["pct_hbm_peak"] = 100 * nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS
+        else:
+            line["bound"] = "mfma"
+        return line
 
     # dense prefill at N=4096 (the shorter dense workload)
     log("dense prefill at N=4096")

@@ -131,6 +131,31 @@ __device__ __forceinline__ void qk_tile(const lds_char* kl, const bf16x8 (&qf)[D
         }
 }
 
+// qk_tile with a fixed schedule: each K read is issued two MFMAs ahead of its use, and hard scheduling barriers keep
+// that order. In the single-buffered walk this measured 2-4% faster than the compiler's own order, bit for bit the
+// same result; the paged and double-buffered walks keep the compiler's order (there it needs more registers).
+template <int D>
+__device__ __forceinline__ void qk_tile_sched(const lds_char* kl, const bf16x8 (&qf)[D / 16], f32x16 (&s)[2], int lane) {
+    constexpr int NQK = D / 8;   // (D / 16) k-steps x 2 key halves
+    constexpr int AH = 2;
+    const int hi = lane >> 5, ln = lane & 31;
+    auto kread = [&](int i) {
+        const int ks = i >> 1, r = 32 * (i & 1) + ln;
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kl + r * Lds<D>::KSTR + (2 * ks + hi) * 16);
+    };
+    bf16x8 kf[NQK];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < AH; ++i) kf[i] = kread(i);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+        if (i + AH < NQK) kf[i + AH] = kread(i + AH);
+        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], s[i & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 __device__ __forceinline__ float pair_max(float x) {
     // lanes l and l^32 hold the two halves of one query row's keys
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -241,6 +266,36 @@ __device__ __forceinline__ void pv_tile(const lds_char* vl, const VtAddr<D>& va,
                 st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, st.o[dt], 0, 0, 0);
             }
         }
+}
+
+// pv_tile with the same fixed schedule: the two transposed reads of each MFMA's A operand are issued two MFMAs ahead.
+template <int D>
+__device__ __forceinline__ void pv_tile_sched(const lds_char* vl, const VtAddr<D>& va, const uint32_t (&pw)[2][8],
+                                        RowState<D>& st) {
+    constexpr int NPV = D / 8;   // 2 key halves x 2 16-key slices x (D / 32) head-dim tiles
+    constexpr int AH = 2;
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    auto vread = [&](int j, v4i16& lo, v4i16& hi4) {
+        const int t = j / (2 * (D / 32)), u = (j / (D / 32)) & 1, dt = j % (D / 32);
+        const int key = 32 * t + 16 * u + va.key_lo, d = 32 * dt + va.dq;
+        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + va.at(key, d)));
+        hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + va.at(key + 8, d)));
+    };
+    v4i16 vlo[NPV], vhi[NPV];
+#pragma unroll
+    for (int j = 0; j < AH; ++j) vread(j, vlo[j], vhi[j]);
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) {
+        if (j + AH < NPV) vread(j + AH, vlo[j + AH], vhi[j + AH]);
+        const int t = j / (2 * (D / 32)), u = (j / (D / 32)) & 1, dt = j % (D / 32);
+        const bf16x8 b = __builtin_bit_cast(
+            bf16x8, (u32x4{pw[t][4 * u], pw[t][4 * u + 1], pw[t][4 * u + 2], pw[t][4 * u + 3]}));
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, (u32x4{__builtin_bit_cast(u32x2, vlo[j])[0], __builtin_bit_cast(u32x2, vlo[j])[1],
+                           __builtin_bit_cast(u32x2, vhi[j])[0], __builtin_bit_cast(u32x2, vhi[j])[1]}));
+        st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, st.o[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // Steady-state tile with a fixed schedule: tile j's softmax, tile j+1's QK and tile j's PV in one stream of steps
@@ -452,11 +507,11 @@ __device__ __forceinline__ void attend_sb(const lds_char* kl, const lds_char* vl
         __syncthreads();
         f32x16 s[2];
         uint32_t pw[2][8];
-        qk_tile<D>(kl, qf, s, lane);
+        qk_tile_sched<D>(kl, qf, s, lane);
         __syncthreads();   // every wave is done with K(j)
         if (j + 1 < ntiles) ld.k.load(krs, (lds_char*)kl, kv_n);
         softmax_tile<D>(s, pw, st, c2, kv + kBN - 1 > q0, kv, qrow, lane);
-        pv_tile<D>(vl, va, pw, st);
+        pv_tile_sched<D>(vl, va, pw, st);
         __syncthreads();   // and with V(j)
         if (j + 1 < ntiles) ld.v.load(vrs, (lds_char*)vl, kv_n);
         kv = kv_n;
