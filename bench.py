@@ -55,6 +55,28 @@ def measured_traffic(key, source):
         return None
 
 
+def device_peak():
+    """The bf16 MFMA peak the device itself implies: compute units x 4096 flop per clock x the peak engine clock the
+    HIP runtime reports (hipDeviceAttributeClockRate, kHz), beside the nominal figure the fractions use. The runtime
+    is the one torch already loaded (found in this process's mappings), so no second copy is opened."""
+    import ctypes
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    out = {"name": props.name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+           "peak_clock_mhz": None, "bf16_peak_from_props_tflops": None}
+    try:
+        path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l and l.split()[-1].startswith("/"))
+        hip = ctypes.CDLL(path)
+        v = ctypes.c_int(0)
+        kHipDeviceAttributeClockRate = 5   # position in hipDeviceAttribute_t (hip_runtime_api.h)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), kHipDeviceAttributeClockRate, torch.cuda.current_device()) == 0:
+            out["peak_clock_mhz"] = v.value / 1e3
+            out["bf16_peak_from_props_tflops"] = props.multi_processor_count * 4096 * v.value * 1e3 / 1e12
+    except (StopIteration, OSError, AttributeError):
+        pass
+    return out
+
+
 def dense_flops(B, Hq, N, D):
     return 2.0 * B * Hq * N * N * D
 
@@ -496,6 +518,7 @@ def main():
                      "kernel": "prefill_dense_kernel<128>", "per_launch_flop": fl_head,
                      "algorithmic_bytes": float((B * Hq + 2 * ch.k.shape[1]) * N * D * 2 + B * Hq * N * D * 2)},
         "cpu_baseline": cpu,
+        "device": device_peak(),
         "paths": paths,
     }
     print(json.dumps(line), flush=True)
