@@ -133,7 +133,7 @@ __device__ __forceinline__ void qk_tile(const lds_char* kl, const bf16x8 (&qf)[D
 
 // qk_tile with a fixed schedule: each K read is issued two MFMAs ahead of its use, and hard scheduling barriers keep
 // that order. In the single-buffered walk this measured 2-4% faster than the compiler's own order, bit for bit the
-// same result; the paged and double-buffered walks keep the compiler's order (there it needs more registers).
+// same result. The paged walk keeps the compiler's order: with this one its D = 128 kernel spills registers.
 template <int D>
 __device__ __forceinline__ void qk_tile_sched(const lds_char* kl, const bf16x8 (&qf)[D / 16], f32x16 (&s)[2], int lane) {
     constexpr int NQK = D / 8;   // (D / 16) k-steps x 2 key halves
