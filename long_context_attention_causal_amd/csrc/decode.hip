@@ -297,7 +297,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const CombineArgs a
     constexpr int LPR = D / 4;      // lanes per partial row
     constexpr int RPL = 64 / LPR;   // partial rows per wave load
     constexpr int NL = 64 / RPL;    // loads per group of 64 chunks
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // wave-uniform (sequence, head): its length is a scalar load and the partial rows' buffer views stay scalar
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int bh = blockIdx.x * 4 + w;
     if (bh >= a.B * a.Hq) return;
     const int b = bh / a.Hq, h = bh % a.Hq;
@@ -314,6 +315,18 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const CombineArgs a
         return;
     }
     const int rr = lane / LPR, dq = 4 * (lane % LPR);
+    // the rows of a group of 64 chunks, requested at once (those of the first group before the maximum is known)
+    auto load_rows = [&](int c0, f32x4 (&v)[NL]) {
+        const int rows = min(64, nc - c0);
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(op + (size_t)c0 * hs * D), (short)0, ((rows - 1) * hs * D + D) * 4, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            v[i] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((RPL * i + rr) * hs * D + dq) * 4, 0, 0));
+    };
+    f32x4 v[NL];
+    load_rows(0, v);
     const float lp0 = lane < nc ? lp[(size_t)lane * hs] : -INFINITY;
     float M = lp0;
     for (int c0 = 64; c0 < nc; c0 += 64) M = fmaxf(M, c0 + lane < nc ? lp[(size_t)(c0 + lane) * hs] : -INFINITY);
@@ -321,14 +334,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const CombineArgs a
     f32x4 acc = f32x4{};
     float sw = 0.0f;
     for (int c0 = 0; c0 < nc; c0 += 64) {
-        const int rows = min(64, nc - c0);
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(op + (size_t)c0 * hs * D), (short)0, ((rows - 1) * hs * D + D) * 4, 0x00020000);
-        f32x4 v[NL];
-#pragma unroll
-        for (int i = 0; i < NL; ++i)
-            v[i] = __builtin_bit_cast(
-                f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((RPL * i + rr) * hs * D + dq) * 4, 0, 0));
+        if (c0 > 0) load_rows(c0, v);
         const float lv = c0 == 0 ? lp0 : (c0 + lane < nc ? lp[(size_t)(c0 + lane) * hs] : -INFINITY);
         const float wl = lv == -INFINITY ? 0.0f : expf(lv - M);
         sw += wl;

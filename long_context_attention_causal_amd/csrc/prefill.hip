@@ -834,7 +834,10 @@ void prefill_sparse_bf16_kernel(const SparseArgs a) {
     __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::VTILE];
     __shared__ __attribute__((aligned(1024))) char v1[Lds<D>::VTILE];
     const Tiles<D> tl{{(lds_char*)k0, (lds_char*)k1}, {(lds_char*)v0, (lds_char*)v1}};
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave-uniform for the single-buffered walk, so its tile offsets stay in scalar registers (marked so in the
+    // eight-wave kernel, the compiler's schedule of the double-buffered walk spills)
+    const int w = NW <= 4 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
     const int per = a.B * a.Hq;
     const int i = a.nb - 1 - (int)(blockIdx.x / per);
     int rest = (int)(blockIdx.x % per);
@@ -868,9 +871,11 @@ void prefill_sparse_bf16_kernel(const SparseArgs a) {
     for (int e = tid; e < cnt; e += NW * 64) lst[e] = list[e];
     __syncthreads();
     const int blk = a.block;
+    // a tile's first key comes from LDS, which the compiler takes as per-lane; read out once as wave-uniform, so the
+    // direct loads get it as their scalar offset instead of looping over lanes for it
+    auto kv_of = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[t / sub] * blk + (t % sub) * kBN); };
     if constexpr (NW <= 4)
-        attend_sb<D, NW>(tl.k[0], tl.v[0], krs, vrs, ntiles, [&](int t) { return lst[t / sub] * blk + (t % sub) * kBN; },
-                         qf, st, a.c2, q0, w, lane);
+        attend_sb<D, NW>(tl.k[0], tl.v[0], krs, vrs, ntiles, kv_of, qf, st, a.c2, q0, w, lane);
     else
         attend<D, NW>(tl, krs, vrs, ntiles, [&](int t) { return lst[t / sub] * blk + (t % sub) * kBN; }, qf, st, a.c2,
                       q0, q0 + 31, w, lane);
