@@ -167,7 +167,8 @@ __device__ double interp7(double xlo, double xhi, long num, bool has_next) {
 __global__ __launch_bounds__(256) void mask_rank_kernel(const ThreshArgs a) {
     __shared__ double rs[4096];
     __shared__ int cnt[2][4][64];
-    const int bg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = a.nb;
+    const int bg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, n = a.nb;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const double* r = a.radius + (size_t)bg * n;
     for (int e = tid; e < n; e += 256) rs[e] = r[e];
     __syncthreads();
@@ -254,7 +255,8 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mask_scores_kernel(const ScoreArgs a) {
     __shared__ double As[kST * kSP];
     __shared__ double Bs[kST * kSP];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int R = a.G * a.nb;
     const int nct = (a.nb + kST - 1) / kST, nrt = (R + kST - 1) / kST;
     const int total = (int)gridDim.x, L = (int)blockIdx.x;
@@ -356,7 +358,8 @@ __device__ __forceinline__ uint64_t order_key(double x) {
 
 template <int E>
 __global__ __launch_bounds__(256) void mask_select_kernel(const SelectArgs a) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // wave-uniform row: its length, budget and the search's branches stay scalar
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const long row = (long)blockIdx.x * 4 + w;
     if (row >= (long)a.B * a.Hq * a.nb) return;   // no barriers in this kernel
     const int i = (int)(row % a.nb);

@@ -784,7 +784,7 @@ template <int D>
 __global__ __launch_bounds__(256) void prefill_paged_combine_kernel(const PagedCombineArgs a) {
     constexpr int PER = D / 64;
     const int lane = threadIdx.x & 63;
-    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long row = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= a.rows) return;
     float M = -INFINITY;
     for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, a.lpart[sp * a.rows + row]);
