@@ -770,7 +770,8 @@ void prefill_paged_kernel(const PagedArgs a) {
     }
 }
 
-// Merge of the key-range splits: one wave per (b, h, row), lane i holding D / 64 head dims.
+// Merge of the key-range splits: each lane merges four head dims of one (b, h, row) with 16-byte loads of the
+// fp32 partials, so a wave covers 256 / D rows.
 struct PagedCombineArgs {
     const float* opart;
     const float* lpart;
@@ -782,30 +783,30 @@ struct PagedCombineArgs {
 
 template <int D>
 __global__ __launch_bounds__(256) void prefill_paged_combine_kernel(const PagedCombineArgs a) {
-    constexpr int PER = D / 64;
+    constexpr int LPR = D / 4;      // lanes per row, four head dims (16 bytes of a partial row) each
+    constexpr int RPW = 64 / LPR;   // rows per wave
     const int lane = threadIdx.x & 63;
-    const long row = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (row >= a.rows) return;
+    const long row = ((long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * RPW + lane / LPR;
+    if (row >= a.rows) return;   // no barriers in this kernel
+    const int d = 4 * (lane % LPR);
     float M = -INFINITY;
     for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, a.lpart[sp * a.rows + row]);
-    float acc[PER] = {};
+    f32x4 acc = f32x4{};
     float wsum = 0.0f;
     for (int sp = 0; sp < a.splits; ++sp) {
         const float ls = a.lpart[sp * a.rows + row];
         const float w = ls == -INFINITY ? 0.0f : __expf(ls - M);
         wsum += w;
-        const float* src = a.opart + ((size_t)sp * a.rows + row) * D + PER * lane;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(a.opart + ((size_t)sp * a.rows + row) * D + d);
 #pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] += w * src[j];
+        for (int j = 0; j < 4; ++j) acc[j] += w * v[j];
     }
     const float inv = 1.0f / wsum;
-    uint16_t* dst = a.o + (size_t)row * D + PER * lane;
-    if constexpr (PER == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    } else {
-        dst[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.0f) & 0xFFFFu);
-    }
-    if (a.lse && lane == 0) a.lse[row] = M + __logf(wsum);
+    u32x2 out;
+    out[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    out[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<u32x2*>(a.o + (size_t)row * D + d) = out;
+    if (a.lse && lane % LPR == 0) a.lse[row] = M + __logf(wsum);
 }
 
 struct SparseArgs {
@@ -1032,7 +1033,8 @@ hipError_t launch_prefill_paged(const PagedPrefillProblem& p, hipStream_t s) {
     c.lse = p.lse;
     c.rows = (long)p.B * p.Hq * p.Nq;
     c.splits = p.splits;
-    const dim3 g2((unsigned)((c.rows + 3) / 4));
+    const long rows_per_wg = 4L * (256 / p.D);   // four waves of 256 / D rows
+    const dim3 g2((unsigned)((c.rows + rows_per_wg - 1) / rows_per_wg));
     if (p.D == 128) hipLaunchKernelGGL((prefill_paged_combine_kernel<128>), g2, dim3(256), 0, s, c);
     else hipLaunchKernelGGL((prefill_paged_combine_kernel<64>), g2, dim3(256), 0, s, c);
     return hipGetLastError();
