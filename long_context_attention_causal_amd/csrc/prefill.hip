@@ -69,9 +69,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base
 // moves 1 KiB into consecutive LDS bytes, lane l's 16 bytes to position l; the lane fetches the global chunk that
 // lands there (a padding slot re-reads a chunk of the same row, so it costs no extra memory traffic). Buffer range
 // checking returns zeros for keys outside [0, N) (including negative tile starts).
-template <int D, int NW, int STR>
+// A tile of BN rows whose bytes are not a whole number of loads gets one more load; its lanes past the last row
+// carry an offset beyond any buffer (no fetch; the LDS bytes they fill lie in the tile's rounded-up allocation).
+template <int D, int NW, int STR, int BN = kBN>
 struct TileLoader {
-    static constexpr int LOADS = kBN * STR / 1024;
+    static constexpr int LOADS = (BN * STR + 1023) / 1024;
     static constexpr int PER = (LOADS + NW - 1) / NW;
     static constexpr int SPR = STR / 16;   // 16-byte slots per LDS row
     int voff[PER];
@@ -83,6 +85,8 @@ struct TileLoader {
             const int z = (first + i) * 64 + lane;   // 16-byte slot inside the tile
             const int r = z / SPR, c = z % SPR;
             voff[i] = r * Lds<D>::ROWB + min(c, Lds<D>::CPR - 1) * 16;
+            if constexpr (BN * STR % 1024 != 0)
+                if (r >= BN) voff[i] = (int)0x80000000u;   // with soff < 2^31 the sum stays past the buffer end
         }
     }
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, lds_char* tile, int kv0) const {
@@ -95,10 +99,10 @@ struct TileLoader {
     }
 };
 
-template <int D, int NW>
+template <int D, int NW, int BN = kBN>
 struct Loaders {
-    TileLoader<D, NW, Lds<D>::KSTR> k;
-    TileLoader<D, NW, Lds<D>::VSTR> v;
+    TileLoader<D, NW, Lds<D>::KSTR, BN> k;
+    TileLoader<D, NW, Lds<D>::VSTR, BN> v;
     __device__ __forceinline__ void init(int w, int lane) {
         k.init(w, lane);
         v.init(w, lane);
@@ -134,24 +138,26 @@ __device__ __forceinline__ void qk_tile(const lds_char* kl, const bf16x8 (&qf)[D
 // qk_tile with a fixed schedule: each K read is issued two MFMAs ahead of its use, and hard scheduling barriers keep
 // that order. In the single-buffered walk this measured 2-4% faster than the compiler's own order, bit for bit the
 // same result. The paged walk keeps the compiler's order: with this one its D = 128 kernel spills registers.
-template <int D>
-__device__ __forceinline__ void qk_tile_sched(const lds_char* kl, const bf16x8 (&qf)[D / 16], f32x16 (&s)[2], int lane) {
-    constexpr int NQK = D / 8;   // (D / 16) k-steps x 2 key halves
+// T2 is the tile's number of 32-key halves (2 for 64-key tiles, 1 for 32-key tiles).
+template <int D, int T2 = 2>
+__device__ __forceinline__ void qk_tile_sched(const lds_char* kl, const bf16x8 (&qf)[D / 16], f32x16 (&s)[T2],
+                                              int lane) {
+    constexpr int NQK = (D / 16) * T2;   // (D / 16) k-steps x T2 key halves
     constexpr int AH = 2;
     const int hi = lane >> 5, ln = lane & 31;
     auto kread = [&](int i) {
-        const int ks = i >> 1, r = 32 * (i & 1) + ln;
+        const int ks = i / T2, r = 32 * (i % T2) + ln;
         return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kl + r * Lds<D>::KSTR + (2 * ks + hi) * 16);
     };
     bf16x8 kf[NQK];
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < T2; ++t) s[t] = f32x16{};
 #pragma unroll
     for (int i = 0; i < AH; ++i) kf[i] = kread(i);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
         if (i + AH < NQK) kf[i + AH] = kread(i + AH);
-        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], s[i & 1], 0, 0, 0);
+        s[i % T2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i / T2], s[i % T2], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -169,13 +175,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 // Online-softmax update for one tile, first half: element mask on a diagonal tile, row max, lazy refresh of the
 // running max (rescaling O and the sum when it moves by more than kSlack). Returns the exp2 bias.
-template <int D>
-__device__ __forceinline__ float softmax_max(f32x16 (&s)[2], RowState<D>& st, float c2, bool diag, int kv0, int qrow,
+template <int D, int T2 = 2>
+__device__ __forceinline__ float softmax_max(f32x16 (&s)[T2], RowState<D>& st, float c2, bool diag, int kv0, int qrow,
                                              int lane) {
     const int hi = lane >> 5;
     if (diag) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < T2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -186,8 +192,10 @@ __device__ __forceinline__ float softmax_max(f32x16 (&s)[2], RowState<D>& st, fl
 #pragma unroll
     for (int k = 0; k < 4; ++k) c[k] = fmaxf(fmaxf(s[0][k], s[0][k + 4]), fmaxf(s[0][k + 8], s[0][k + 12]));
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        c[k] = fmaxf(c[k], fmaxf(fmaxf(s[1][k], s[1][k + 4]), fmaxf(s[1][k + 8], s[1][k + 12])));
+    for (int t = 1; t < T2; ++t)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            c[k] = fmaxf(c[k], fmaxf(fmaxf(s[t][k], s[t][k + 4]), fmaxf(s[t][k + 8], s[t][k + 12])));
     const float mx = pair_max(fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])));
     const float mxs = mx * c2;
     if (mxs > st.m + kSlack) {
@@ -202,7 +210,8 @@ __device__ __forceinline__ float softmax_max(f32x16 (&s)[2], RowState<D>& st, fl
 
 // Second half, one slice: the two probabilities of accumulator slots 2w and 2w+1 of key half t, rounded to bf16 and
 // packed in the B-operand order of the PV product; their sum (of the rounded values) goes into l.
-__device__ __forceinline__ void softmax_slice(const f32x16 (&s)[2], uint32_t (&pw)[2][8], int t, int w, float c2,
+template <int T2 = 2>
+__device__ __forceinline__ void softmax_slice(const f32x16 (&s)[T2], uint32_t (&pw)[T2][8], int t, int w, float c2,
                                               float bias, float& l) {
     bf16x2 ones;
     ones[0] = (__bf16)1.0f;
@@ -214,15 +223,15 @@ __device__ __forceinline__ void softmax_slice(const f32x16 (&s)[2], uint32_t (&p
 }
 
 // Whole online-softmax update for one tile.
-template <int D>
-__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], uint32_t (&pw)[2][8], RowState<D>& st, float c2,
+template <int D, int T2 = 2>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[T2], uint32_t (&pw)[T2][8], RowState<D>& st, float c2,
                                              bool diag, int kv0, int qrow, int lane) {
-    const float bias = softmax_max<D>(s, st, c2, diag, kv0, qrow, lane);
+    const float bias = softmax_max<D, T2>(s, st, c2, diag, kv0, qrow, lane);
     float l0 = 0.0f, l1 = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < T2; ++t)
 #pragma unroll
-        for (int w = 0; w < 8; ++w) softmax_slice(s, pw, t, w, c2, bias, (w & 1) ? l1 : l0);
+        for (int w = 0; w < 8; ++w) softmax_slice<T2>(s, pw, t, w, c2, bias, (w & 1) ? l1 : l0);
     st.l += l0 + l1;
 }
 
@@ -269,10 +278,10 @@ __device__ __forceinline__ void pv_tile(const lds_char* vl, const VtAddr<D>& va,
 }
 
 // pv_tile with the same fixed schedule: the two transposed reads of each MFMA's A operand are issued two MFMAs ahead.
-template <int D>
-__device__ __forceinline__ void pv_tile_sched(const lds_char* vl, const VtAddr<D>& va, const uint32_t (&pw)[2][8],
-                                        RowState<D>& st) {
-    constexpr int NPV = D / 8;   // 2 key halves x 2 16-key slices x (D / 32) head-dim tiles
+template <int D, int T2 = 2>
+__device__ __forceinline__ void pv_tile_sched(const lds_char* vl, const VtAddr<D>& va, const uint32_t (&pw)[T2][8],
+                                              RowState<D>& st) {
+    constexpr int NPV = T2 * (D / 16);   // T2 key halves x 2 16-key slices x (D / 32) head-dim tiles
     constexpr int AH = 2;
     typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
     auto vread = [&](int j, v4i16& lo, v4i16& hi4) {
@@ -488,12 +497,13 @@ struct DenseArgs {
 // as every wave has finished this tile's QK product (it lands during the softmax and PV), the next V tile once PV is
 // done. With half the LDS of the double-buffered walk, twice as many work-groups share a CU (two waves per SIMD
 // instead of one for 64-row blocks) and cover each other's load latency.
-template <int D, int NW, typename KvOf>
+template <int D, int NW, typename KvOf, int T2 = 2>
 __device__ __forceinline__ void attend_sb(const lds_char* kl, const lds_char* vl, __amdgpu_buffer_rsrc_t krs,
                                           __amdgpu_buffer_rsrc_t vrs, int ntiles, KvOf kv_of,
                                           const bf16x8 (&qf)[D / 16], RowState<D>& st, float c2, int q0, int w,
                                           int lane) {
-    Loaders<D, NW> ld;
+    constexpr int BN = 32 * T2;   // keys per tile
+    Loaders<D, NW, BN> ld;
     ld.init(w, lane);
     VtAddr<D> va;
     va.init(lane);
@@ -505,13 +515,13 @@ __device__ __forceinline__ void attend_sb(const lds_char* kl, const lds_char* vl
         const int kv_n = j + 1 < ntiles ? kv_of(j + 1) : 0;
         wait_vmem();
         __syncthreads();
-        f32x16 s[2];
-        uint32_t pw[2][8];
-        qk_tile_sched<D>(kl, qf, s, lane);
+        f32x16 s[T2];
+        uint32_t pw[T2][8];
+        qk_tile_sched<D, T2>(kl, qf, s, lane);
         __syncthreads();   // every wave is done with K(j)
         if (j + 1 < ntiles) ld.k.load(krs, (lds_char*)kl, kv_n);
-        softmax_tile<D>(s, pw, st, c2, kv + kBN - 1 > q0, kv, qrow, lane);
-        pv_tile_sched<D>(vl, va, pw, st);
+        softmax_tile<D, T2>(s, pw, st, c2, kv + BN - 1 > q0, kv, qrow, lane);
+        pv_tile_sched<D, T2>(vl, va, pw, st);
         __syncthreads();   // and with V(j)
         if (j + 1 < ntiles) ld.v.load(vrs, (lds_char*)vl, kv_n);
         kv = kv_n;
@@ -828,11 +838,15 @@ struct SparseArgs {
 // share a CU (two and three waves per SIMD; the four-wave kernel is held to the register budget of three).
 // Eight-wave work-groups keep the double-buffered one-phase step.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 3 : 2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 4 ? 3 : 2)))
 void prefill_sparse_bf16_kernel(const SparseArgs a) {
-    __shared__ __attribute__((aligned(1024))) char k0[Lds<D>::KTILE];
+    // 64-row blocks walk 32-key tiles: 21 KB of LDS per work-group, so six of them (three waves per SIMD) share a CU
+    constexpr int T2 = NW == 2 ? 1 : 2;   // 32-key halves per tile
+    constexpr int BN = 32 * T2;
+    constexpr int KT = (BN * Lds<D>::KSTR + 1023) / 1024 * 1024, VT = (BN * Lds<D>::VSTR + 1023) / 1024 * 1024;
+    __shared__ __attribute__((aligned(1024))) char k0[KT];
     __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::KTILE];
-    __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::VTILE];
+    __shared__ __attribute__((aligned(1024))) char v0[VT];
     __shared__ __attribute__((aligned(1024))) char v1[Lds<D>::VTILE];
     const Tiles<D> tl{{(lds_char*)k0, (lds_char*)k1}, {(lds_char*)v0, (lds_char*)v1}};
     const int tid = threadIdx.x, lane = tid & 63;
@@ -853,7 +867,7 @@ void prefill_sparse_bf16_kernel(const SparseArgs a) {
     const size_t row = ((size_t)b * a.Hq + h) * a.nb + i;
     const int cnt = a.kv_count[row];
     const int32_t* list = a.kv_index + row * a.nb;
-    const int sub = a.block / kBN;
+    const int sub = a.block / BN;
     const int ntiles = cnt * sub;
 
     const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)a.N * D;
@@ -874,9 +888,9 @@ void prefill_sparse_bf16_kernel(const SparseArgs a) {
     const int blk = a.block;
     // a tile's first key comes from LDS, which the compiler takes as per-lane; read out once as wave-uniform, so the
     // direct loads get it as their scalar offset instead of looping over lanes for it
-    auto kv_of = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[t / sub] * blk + (t % sub) * kBN); };
+    auto kv_of = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[t / sub] * blk + (t % sub) * BN); };
     if constexpr (NW <= 4)
-        attend_sb<D, NW>(tl.k[0], tl.v[0], krs, vrs, ntiles, kv_of, qf, st, a.c2, q0, w, lane);
+        attend_sb<D, NW, decltype(kv_of), T2>(tl.k[0], tl.v[0], krs, vrs, ntiles, kv_of, qf, st, a.c2, q0, w, lane);
     else
         attend<D, NW>(tl, krs, vrs, ntiles, [&](int t) { return lst[t / sub] * blk + (t % sub) * kBN; }, qf, st, a.c2,
                       q0, q0 + 31, w, lane);

@@ -260,7 +260,10 @@ def test_sparse_all_blocks_equals_dense(lib, block):
     Oref, _ = A.causal_attention(*inp.as_f64(), inp.scale)
     assert max_err(host64(o), Oref) <= BF16_TOL
     assert (o.float() - od.float()).abs().max().item() <= BF16_TOL
-    assert (lse - ld).abs().max().item() <= 1e-3
+    # 128-row blocks walk the dense kernel's 64-key tiles, so both paths round the same probabilities; 64-row blocks
+    # walk 32-key tiles, whose running maxima (hence the bf16 roundings in the row sums) can differ from the dense
+    # walk's: two independently rounded sums, each within 2^-8 relative, agree in ln l to 2 * 2^-8
+    assert (lse - ld).abs().max().item() <= (1e-3 if block == 128 else 2 * 2.0 ** -8)
 
 
 @pytest.mark.parametrize("mode", [0, 1])
