@@ -6,7 +6,7 @@
 // rescaled whenever the max moves, so the score matrix never leaves the chip and the result equals plain
 // softmax attention up to rounding.
 //
-// bf16 tile body (one wave = 32 query rows of one head, one KV tile = 64 keys):
+// bf16 tile body (one wave = 32 query rows of one head, one KV tile = 64 keys, or 32 for 64-row sparse blocks):
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = the wave's Q rows held in VGPRs for
 //   the whole work-group. In the 32x32 accumulator layout lane l owns query column l%32 and 16 keys, so a row
 //   max/sum is 15 in-lane ops plus one exchange with lane l^32.
@@ -834,8 +834,8 @@ struct SparseArgs {
 // Work-group = one (batch, head, query block); NW = block / 32 waves. The tile loop walks the row's kept-block
 // list (ascending, so the diagonal block, the only one needing an element mask, comes last); skipped blocks
 // are never read. Rows are issued latest block first, as they tend to hold the longest lists. Work-groups of two
-// and four waves (64- and 128-row blocks) walk with one buffer per tile: the LDS saved lets 4 and 3 work-groups
-// share a CU (two and three waves per SIMD; the four-wave kernel is held to the register budget of three).
+// and four waves (64- and 128-row blocks) walk with one buffer per tile, the two-wave ones over 32-key tiles: the
+// LDS saved lets 6 and 3 work-groups share a CU (three waves per SIMD, the register budget both are held to).
 // Eight-wave work-groups keep the double-buffered one-phase step.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 4 ? 3 : 2)))
