@@ -19,11 +19,10 @@
 //   The row sum adds the bf16-rounded probabilities (v_dot2_f32_bf16), i.e. exactly the weights the PV
 //   product uses.
 // Staging: K and V tiles go from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane, no staging
-// registers) into one of two buffers while the other is in use.
-// Schedules: dense work-groups and block-sparse ones of up to 128 rows walk their tiles single-buffered (QK, softmax,
-// PV per tile; the next K tile requested once every wave is done with the current one), small enough in LDS and
-// registers that several work-groups share each CU and overlap each other; 256-row block-sparse work-groups run one
-// double-buffered phase per tile in each wave (the next tile's QK MFMAs interleaved with this tile's softmax).
+// registers).
+// Schedule: every work-group walks its tiles single-buffered (QK, softmax, PV per tile; the next K tile requested
+// once every wave is done with the current one, the next V tile once PV is done), small enough in LDS and registers
+// that several work-groups share each CU and overlap each other's loads, softmax and MFMA streams.
 // The file is compiled without NaN semantics (see the build script): a max then needs no quieting of its inputs.
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -118,27 +117,11 @@ struct RowState {
     float l;  // this lane's share of the row sum
 };
 
-// S^T for a 64-key tile: two 32x32 blocks (keys x this wave's 32 query rows); the two accumulators alternate.
-template <int D>
-__device__ __forceinline__ void qk_tile(const lds_char* kl, const bf16x8 (&qf)[D / 16], f32x16 (&s)[2], int lane) {
-    const int hi = lane >> 5, ln = lane & 31;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int r = 32 * t + ln;
-            const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-                kl + r * Lds<D>::KSTR + (2 * ks + hi) * 16);
-            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
-        }
-}
-
-// qk_tile with a fixed schedule: each K read is issued two MFMAs ahead of its use, and hard scheduling barriers keep
-// that order. In the single-buffered walk this measured 2-4% faster than the compiler's own order, bit for bit the
-// same result. The paged walk keeps the compiler's order: with this one its D = 128 kernel spills registers.
-// T2 is the tile's number of 32-key halves (2 for 64-key tiles, 1 for 32-key tiles).
+// S^T for one tile: T2 32x32 blocks (keys x this wave's 32 query rows; T2 = 2 for 64-key tiles, 1 for 32-key
+// tiles), accumulated alternately. Fixed schedule: each K read is issued two MFMAs ahead of its use, and hard
+// scheduling barriers keep that order; this measured 2-4% faster than the compiler's own order, bit for bit the
+// same result. The paged kernel's swizzled variant below keeps the compiler's order: with this one its D = 128
+// kernel spills registers.
 template <int D, int T2 = 2>
 __device__ __forceinline__ void qk_tile_sched(const lds_char* kl, const bf16x8 (&qf)[D / 16], f32x16 (&s)[T2],
                                               int lane) {
@@ -252,7 +235,7 @@ struct VtAddr {
     }
 };
 
-// O^T += V^T P^T over the tile's 64 keys.
+// O^T += V^T P^T over a 64-key tile in the compiler's order (the paged walk).
 template <int D>
 __device__ __forceinline__ void pv_tile(const lds_char* vl, const VtAddr<D>& va, const uint32_t (&pw)[2][8],
                                         RowState<D>& st) {
@@ -277,74 +260,13 @@ __device__ __forceinline__ void pv_tile(const lds_char* vl, const VtAddr<D>& va,
         }
 }
 
-// pv_tile with the same fixed schedule: the two transposed reads of each MFMA's A operand are issued two MFMAs ahead.
+// O^T += V^T P^T with the fixed schedule of qk_tile_sched: the two transposed reads of each MFMA's A operand are
+// issued two MFMAs ahead.
 template <int D, int T2 = 2>
 __device__ __forceinline__ void pv_tile_sched(const lds_char* vl, const VtAddr<D>& va, const uint32_t (&pw)[T2][8],
                                               RowState<D>& st) {
     constexpr int NPV = T2 * (D / 16);   // T2 key halves x 2 16-key slices x (D / 32) head-dim tiles
     constexpr int AH = 2;
-    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-    auto vread = [&](int j, v4i16& lo, v4i16& hi4) {
-        const int t = j / (2 * (D / 32)), u = (j / (D / 32)) & 1, dt = j % (D / 32);
-        const int key = 32 * t + 16 * u + va.key_lo, d = 32 * dt + va.dq;
-        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + va.at(key, d)));
-        hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + va.at(key + 8, d)));
-    };
-    v4i16 vlo[NPV], vhi[NPV];
-#pragma unroll
-    for (int j = 0; j < AH; ++j) vread(j, vlo[j], vhi[j]);
-#pragma unroll
-    for (int j = 0; j < NPV; ++j) {
-        if (j + AH < NPV) vread(j + AH, vlo[j + AH], vhi[j + AH]);
-        const int t = j / (2 * (D / 32)), u = (j / (D / 32)) & 1, dt = j % (D / 32);
-        const bf16x8 b = __builtin_bit_cast(
-            bf16x8, (u32x4{pw[t][4 * u], pw[t][4 * u + 1], pw[t][4 * u + 2], pw[t][4 * u + 3]}));
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, (u32x4{__builtin_bit_cast(u32x2, vlo[j])[0], __builtin_bit_cast(u32x2, vlo[j])[1],
-                           __builtin_bit_cast(u32x2, vhi[j])[0], __builtin_bit_cast(u32x2, vhi[j])[1]}));
-        st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, st.o[dt], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// Steady-state tile with a fixed schedule: tile j's softmax, tile j+1's QK and tile j's PV in one stream of steps
-// separated by hard scheduling barriers, so the order below is the issue order. QK step i: the K read two MFMAs
-// ahead, the MFMA, and 16 / (D / 8) slices of the softmax on the VALU (they only need the row max, computed
-// first). PV step j: the two transposed reads of the MFMA two ahead, then the MFMA. Every MFMA finds its operands
-// already requested two steps earlier, and the VALU work fills the matrix cores' busy time.
-template <int D>
-__device__ __forceinline__ void steady_tile(const lds_char* kl, const lds_char* vl, const VtAddr<D>& va,
-                                            const bf16x8 (&qf)[D / 16], f32x16 (&scur)[2], f32x16 (&snext)[2],
-                                            uint32_t (&pw)[2][8], RowState<D>& st, float c2, int qrow, int lane) {
-    constexpr int NQK = D / 8;        // (D / 16) k-steps x 2 key halves
-    constexpr int SPQ = 16 / NQK;     // softmax slices per QK MFMA
-    constexpr int NPV = D / 8;        // 2 key halves x 2 16-key slices x (D / 32) head-dim tiles
-    constexpr int AH = 2;             // reads issued this many MFMAs ahead
-    const int hi = lane >> 5, ln = lane & 31;
-    const float bias = softmax_max<D>(scur, st, c2, false, 0, qrow, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    auto kread = [&](int i) {
-        const int ks = i >> 1, r = 32 * (i & 1) + ln;
-        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kl + r * Lds<D>::KSTR + (2 * ks + hi) * 16);
-    };
-    bf16x8 kf[NQK];
-    snext[0] = f32x16{};
-    snext[1] = f32x16{};
-    float l0 = 0.0f, l1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < AH; ++i) kf[i] = kread(i);
-#pragma unroll
-    for (int i = 0; i < NQK; ++i) {
-        if (i + AH < NQK) kf[i + AH] = kread(i + AH);
-        snext[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], snext[i & 1], 0, 0, 0);
-#pragma unroll
-        for (int k = 0; k < SPQ; ++k) {
-            const int sl = i * SPQ + k;
-            softmax_slice(scur, pw, sl >> 3, sl & 7, c2, bias, (sl & 1) ? l1 : l0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    st.l += l0 + l1;
     typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
     auto vread = [&](int j, v4i16& lo, v4i16& hi4) {
         const int t = j / (2 * (D / 32)), u = (j / (D / 32)) & 1, dt = j % (D / 32);
@@ -406,78 +328,6 @@ __device__ __forceinline__ void init_state(RowState<D>& st) {
     st.l = 0.0f;
 }
 
-// LDS of one work-group: two K and two V tiles.
-template <int D>
-struct Tiles {
-    lds_char* k[2];
-    lds_char* v[2];
-};
-
-// The KV loop of one work-group, software-pipelined inside every wave: while the VALU turns tile j's scores
-// into probabilities, the matrix cores already compute tile j+1's scores; then tile j's PV product. K is staged
-// one tile ahead of V so both are resident: during step j LDS holds K(j+1) and V(j), and the step's loads of
-// K(j+2) and V(j+1) stream straight into the buffers step j-1 finished with. One barrier per step; the
-// buffer parity is a compile-time constant inside each unrolled step.
-// kv_of(t) gives tile t's first key; a wave skips tiles that start past its last row, and masks elements only on
-// tiles that reach past its first row.
-template <int D, int NW, int PAR, typename KvOf>
-__device__ __forceinline__ void attend_step(const Tiles<D>& tl, const Loaders<D, NW>& ld,
-                                            __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, const VtAddr<D>& va,
-                                            int j, int ntiles, KvOf kv_of, int& kv_cur, int& kv_nxt,
-                                            const bf16x8 (&qf)[D / 16], f32x16 (&scur)[2], f32x16 (&snext)[2],
-                                            RowState<D>& st, float c2, int q0, int wave_last, int lane) {
-    const int qrow = q0 + (lane & 31);
-    const bool has_next = j + 1 < ntiles;
-    const bool act = kv_cur <= wave_last;
-    const bool act_n = has_next && kv_nxt <= wave_last;
-    const bool diag = kv_cur + kBN - 1 > q0;
-    const int kv_2 = j + 2 < ntiles ? kv_of(j + 2) : 0;
-    if (j + 2 < ntiles) ld.k.load(krs, tl.k[PAR], kv_2);
-    if (has_next) ld.v.load(vrs, tl.v[1 - PAR], kv_nxt);
-    uint32_t pw[2][8];
-    if (act && act_n && !diag) {
-        steady_tile<D>(tl.k[1 - PAR], tl.v[PAR], va, qf, scur, snext, pw, st, c2, qrow, lane);
-    } else {
-        if (act) softmax_tile<D>(scur, pw, st, c2, diag, kv_cur, qrow, lane);
-        if (act_n) qk_tile<D>(tl.k[1 - PAR], qf, snext, lane);
-        if (act) pv_tile<D>(tl.v[PAR], va, pw, st);
-    }
-    wait_vmem();
-    __syncthreads();
-    kv_cur = kv_nxt;
-    kv_nxt = kv_2;
-}
-
-template <int D, int NW, typename KvOf>
-__device__ __forceinline__ void attend(const Tiles<D>& tl, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                       int ntiles, KvOf kv_of, const bf16x8 (&qf)[D / 16], RowState<D>& st, float c2,
-                                       int q0, int wave_last, int w, int lane) {
-    Loaders<D, NW> ld;
-    ld.init(w, lane);
-    VtAddr<D> va;
-    va.init(lane);
-    int kv_cur = kv_of(0);
-    int kv_nxt = ntiles > 1 ? kv_of(1) : 0;
-    ld.k.load(krs, tl.k[0], kv_cur);
-    ld.v.load(vrs, tl.v[0], kv_cur);
-    if (ntiles > 1) ld.k.load(krs, tl.k[1], kv_nxt);
-    wait_vmem();
-    __syncthreads();
-    f32x16 sa[2], sb[2];
-    if (kv_cur <= wave_last) qk_tile<D>(tl.k[0], qf, sa, lane);
-    __syncthreads();
-    int j = 0;
-    for (; j + 1 < ntiles; j += 2) {
-        attend_step<D, NW, 0>(tl, ld, krs, vrs, va, j, ntiles, kv_of, kv_cur, kv_nxt, qf, sa, sb, st, c2, q0,
-                              wave_last, lane);
-        attend_step<D, NW, 1>(tl, ld, krs, vrs, va, j + 1, ntiles, kv_of, kv_cur, kv_nxt, qf, sb, sa, st, c2, q0,
-                              wave_last, lane);
-    }
-    if (j < ntiles)
-        attend_step<D, NW, 0>(tl, ld, krs, vrs, va, j, ntiles, kv_of, kv_cur, kv_nxt, qf, sa, sb, st, c2, q0,
-                              wave_last, lane);
-}
-
 struct DenseArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -493,10 +343,9 @@ struct DenseArgs {
 };
 
 
-// Single-buffered tile walk for small work-groups: one K and one V tile in LDS. The next K tile is requested as soon
-// as every wave has finished this tile's QK product (it lands during the softmax and PV), the next V tile once PV is
-// done. With half the LDS of the double-buffered walk, twice as many work-groups share a CU (two waves per SIMD
-// instead of one for 64-row blocks) and cover each other's load latency.
+// Single-buffered tile walk: one K and one V tile in LDS. The next K tile is requested as soon as every wave has
+// finished this tile's QK product (it lands during the softmax and PV), the next V tile once PV is done. With half
+// the LDS of a double-buffered walk, twice as many work-groups share a CU and cover each other's load latency.
 template <int D, int NW, typename KvOf, int T2 = 2>
 __device__ __forceinline__ void attend_sb(const lds_char* kl, const lds_char* vl, __amdgpu_buffer_rsrc_t krs,
                                           __amdgpu_buffer_rsrc_t vrs, int ntiles, KvOf kv_of,
@@ -834,27 +683,26 @@ struct SparseArgs {
 // Work-group = one (batch, head, query block); NW = block / 32 waves. The tile loop walks the row's kept-block
 // list (ascending, so the diagonal block, the only one needing an element mask, comes last); skipped blocks
 // are never read. Rows are issued latest block first, as they tend to hold the longest lists. Work-groups of two
-// and four waves (64- and 128-row blocks) walk with one buffer per tile, the two-wave ones over 32-key tiles: the
-// LDS saved lets 6 and 3 work-groups share a CU (three waves per SIMD, the register budget both are held to).
-// Eight-wave work-groups keep the double-buffered one-phase step.
+// waves (64-row blocks, over 32-key tiles) and four waves (128-row blocks, and each half of a 256-row block, over
+// 64-key tiles) share a CU six and three at a time (three waves per SIMD, the register budget both are held to).
+// A half of a 256-row block walks its diagonal block only as far as its own last row.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 4 ? 3 : 2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void prefill_sparse_bf16_kernel(const SparseArgs a) {
     // 64-row blocks walk 32-key tiles: 21 KB of LDS per work-group, so six of them (three waves per SIMD) share a CU
     constexpr int T2 = NW == 2 ? 1 : 2;   // 32-key halves per tile
     constexpr int BN = 32 * T2;
     constexpr int KT = (BN * Lds<D>::KSTR + 1023) / 1024 * 1024, VT = (BN * Lds<D>::VSTR + 1023) / 1024 * 1024;
     __shared__ __attribute__((aligned(1024))) char k0[KT];
-    __shared__ __attribute__((aligned(1024))) char k1[Lds<D>::KTILE];
     __shared__ __attribute__((aligned(1024))) char v0[VT];
-    __shared__ __attribute__((aligned(1024))) char v1[Lds<D>::VTILE];
-    const Tiles<D> tl{{(lds_char*)k0, (lds_char*)k1}, {(lds_char*)v0, (lds_char*)v1}};
     const int tid = threadIdx.x, lane = tid & 63;
-    // wave-uniform for the single-buffered walk, so its tile offsets stay in scalar registers (marked so in the
-    // eight-wave kernel, the compiler's schedule of the double-buffered walk spills)
-    const int w = NW <= 4 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile offsets stay in scalar registers
     const int per = a.B * a.Hq;
-    const int i = a.nb - 1 - (int)(blockIdx.x / per);
+    // a query block of more than 32 * NW rows (256-row blocks) is split over `parts` work-groups of 32 * NW rows
+    const int parts = a.block / (32 * NW);
+    const int ib = (int)(blockIdx.x / per);
+    const int i = a.nb - 1 - ib / parts;
+    const int part = parts - 1 - ib % parts;
     int rest = (int)(blockIdx.x % per);
     // work-groups go to the 8 XCDs round-robin; when the heads split evenly, XCD x takes the x-th run of per / 8
     // heads in kv-group order, so its L2 serves as few kv heads as possible
@@ -862,13 +710,12 @@ void prefill_sparse_bf16_kernel(const SparseArgs a) {
     const int h = rest % a.Hq;
     const int b = rest / a.Hq;
     const int g = h / a.G;
-    const int q0 = i * a.block + 32 * w;
+    const int q0 = i * a.block + part * 32 * NW + 32 * w;
     const int qrow = q0 + (lane & 31);
     const size_t row = ((size_t)b * a.Hq + h) * a.nb + i;
     const int cnt = a.kv_count[row];
     const int32_t* list = a.kv_index + row * a.nb;
-    const int sub = a.block / BN;
-    const int ntiles = cnt * sub;
+    const int sub = a.block / BN;   // tiles per key block
 
     const size_t qoff = ((size_t)b * a.Hq + h) * (size_t)a.N * D;
     const size_t kvoff = ((size_t)b * a.Hkv + g) * (size_t)a.N * D;
@@ -879,21 +726,21 @@ void prefill_sparse_bf16_kernel(const SparseArgs a) {
     load_q<D>(qf, a.q + qoff, qrow, a.N, lane);
     RowState<D> st;
     init_state<D>(st);
-    if (ntiles == 0) return;  // every valid list holds the diagonal; an empty one leaves the rows unwritten
+    if (cnt == 0) return;  // every valid list holds the diagonal; an empty one leaves the rows unwritten
     // the row's block list goes to LDS once, so the tile loop reads the next tile's block in LDS latency instead
     // of a global round trip per tile
     extern __shared__ int lst[];   // nb entries, sized at launch
     for (int e = tid; e < cnt; e += NW * 64) lst[e] = list[e];
     __syncthreads();
+    // the diagonal block (the list's last) is walked only up to this work-group's last row
+    const int diag_tiles = ((part + 1) * 32 * NW + BN - 1) / BN;
+    const int ntiles = (cnt - 1) * sub + (lst[cnt - 1] == i ? diag_tiles : sub);
     const int blk = a.block;
     // a tile's first key comes from LDS, which the compiler takes as per-lane; read out once as wave-uniform, so the
     // direct loads get it as their scalar offset instead of looping over lanes for it
     auto kv_of = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[t / sub] * blk + (t % sub) * BN); };
-    if constexpr (NW <= 4)
-        attend_sb<D, NW, decltype(kv_of), T2>(tl.k[0], tl.v[0], krs, vrs, ntiles, kv_of, qf, st, a.c2, q0, w, lane);
-    else
-        attend<D, NW>(tl, krs, vrs, ntiles, [&](int t) { return lst[t / sub] * blk + (t % sub) * kBN; }, qf, st, a.c2,
-                      q0, q0 + 31, w, lane);
+    attend_sb<D, NW, decltype(kv_of), T2>((lds_char*)k0, (lds_char*)v0, krs, vrs, ntiles, kv_of, qf, st, a.c2, q0,
+                                          w, lane);
     finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
 }
 
@@ -1103,18 +950,16 @@ hipError_t launch_prefill_sparse_bf16(const PrefillProblem& p, int block, const 
     a.block = block;
     a.nb = p.N / block;
     a.c2 = p.scale * kLog2e;
-    const dim3 grid((unsigned)(a.nb * a.B * a.Hq));
     const size_t lst_bytes = ((size_t)a.nb * sizeof(int32_t) + 15) / 16 * 16;   // the kept-block list in LDS
-    // one wave per 32 rows of the query block
+    // one wave per 32 rows: two waves for 64-row blocks; four for 128-row blocks, and for each half of a 256-row one
     if (block == 64) {
+        const dim3 grid((unsigned)(a.nb * a.B * a.Hq));
         if (p.D == 128) hipLaunchKernelGGL((prefill_sparse_bf16_kernel<128, 2>), grid, dim3(128), lst_bytes, s, a);
         else hipLaunchKernelGGL((prefill_sparse_bf16_kernel<64, 2>), grid, dim3(128), lst_bytes, s, a);
-    } else if (block == 128) {
+    } else if (block == 128 || block == 256) {
+        const dim3 grid((unsigned)(a.nb * (block / 128) * a.B * a.Hq));
         if (p.D == 128) hipLaunchKernelGGL((prefill_sparse_bf16_kernel<128, 4>), grid, dim3(256), lst_bytes, s, a);
         else hipLaunchKernelGGL((prefill_sparse_bf16_kernel<64, 4>), grid, dim3(256), lst_bytes, s, a);
-    } else if (block == 256) {
-        if (p.D == 128) hipLaunchKernelGGL((prefill_sparse_bf16_kernel<128, 8>), grid, dim3(512), lst_bytes, s, a);
-        else hipLaunchKernelGGL((prefill_sparse_bf16_kernel<64, 8>), grid, dim3(512), lst_bytes, s, a);
     } else {
         return hipErrorInvalidValue;
     }
