@@ -171,15 +171,19 @@ __device__ __forceinline__ float softmax_max(f32x16 (&s)[T2], RowState<D>& st, f
                 if (key > qrow) s[t][r] = -INFINITY;
             }
     }
-    float c[4];
+    // one chain of three-input maxima per key half (v_max3_f32: two values per instruction)
+    float c[T2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) c[k] = fmaxf(fmaxf(s[0][k], s[0][k + 4]), fmaxf(s[0][k + 8], s[0][k + 12]));
+    for (int t = 0; t < T2; ++t) {
+        c[t] = fmaxf(fmaxf(s[t][0], s[t][1]), s[t][2]);
 #pragma unroll
-    for (int t = 1; t < T2; ++t)
+        for (int r = 3; r + 1 < 16; r += 2) c[t] = fmaxf(fmaxf(c[t], s[t][r]), s[t][r + 1]);
+        c[t] = fmaxf(c[t], s[t][15]);
+    }
+    float cm = c[0];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            c[k] = fmaxf(c[k], fmaxf(fmaxf(s[t][k], s[t][k + 4]), fmaxf(s[t][k + 8], s[t][k + 12])));
-    const float mx = pair_max(fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])));
+    for (int t = 1; t < T2; ++t) cm = fmaxf(cm, c[t]);
+    const float mx = pair_max(cm);
     const float mxs = mx * c2;
     if (mxs > st.m + kSlack) {
         const float alpha = __builtin_amdgcn_exp2f(st.m - mxs);
@@ -210,12 +214,12 @@ template <int D, int T2 = 2>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[T2], uint32_t (&pw)[T2][8], RowState<D>& st, float c2,
                                              bool diag, int kv0, int qrow, int lane) {
     const float bias = softmax_max<D, T2>(s, st, c2, diag, kv0, qrow, lane);
-    float l0 = 0.0f, l1 = 0.0f;
+    float l0 = st.l, l1 = 0.0f;
 #pragma unroll
     for (int t = 0; t < T2; ++t)
 #pragma unroll
         for (int w = 0; w < 8; ++w) softmax_slice<T2>(s, pw, t, w, c2, bias, (w & 1) ? l1 : l0);
-    st.l += l0 + l1;
+    st.l = l0 + l1;
 }
 
 // Per-lane byte offsets of the transposed V reads. The A operand of a PV MFMA holds, in lane (ln, hi), the head
