@@ -9,7 +9,7 @@
 // bf16 tile body (one wave = 32 query rows of one head, one KV tile = 64 keys, or 32 for 64-row sparse blocks):
 //   S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = the wave's Q rows held in VGPRs for
 //   the whole work-group. In the 32x32 accumulator layout lane l owns query column l%32 and 16 keys, so a row
-//   max/sum is 15 in-lane ops plus one exchange with lane l^32.
+//   max is an in-lane chain of three-input maxima plus one exchange with lane l^32.
 //   O^T += V^T P^T with the same MFMA: the bf16-rounded probabilities are already in B-operand order in the
 //   lane that computed them (no LDS round trip); V stays in its natural row-major layout in LDS and each A
 //   operand is two ds_read_b64_tr_b16 reads, which transpose 4 keys x 16 head dims per 16-lane group.
