@@ -120,17 +120,21 @@ struct RowState {
 // S^T for one tile: T2 32x32 blocks (keys x this wave's 32 query rows; T2 = 2 for 64-key tiles, 1 for 32-key
 // tiles), accumulated alternately. Fixed schedule: each K read is issued two MFMAs ahead of its use, and hard
 // scheduling barriers keep that order; this measured 2-4% faster than the compiler's own order, bit for bit the
-// same result. The paged kernel's swizzled variant below keeps the compiler's order: with this one its D = 128
-// kernel spills registers.
-template <int D, int T2 = 2>
+// same result. K rows sit KSTR bytes apart, or, for a tile gathered from 16-row pages (PSLOT > 0), in page slots
+// PSLOT bytes apart: row r at (r / 16) * PSLOT + (r % 16) * KSTR. Either way every read is one per-lane base plus a
+// compile-time offset. (The paged kernel's swizzled variant below keeps the compiler's order: with this schedule
+// its D = 128 kernel spills registers.)
+template <int D, int T2 = 2, int PSLOT = 0>
 __device__ __forceinline__ void qk_tile_sched(const lds_char* kl, const bf16x8 (&qf)[D / 16], f32x16 (&s)[T2],
                                               int lane) {
     constexpr int NQK = (D / 16) * T2;   // (D / 16) k-steps x T2 key halves
     constexpr int AH = 2;
     const int hi = lane >> 5, ln = lane & 31;
+    const lds_char* kp = kl + (ln / 16) * PSLOT + (ln % 16) * Lds<D>::KSTR;   // paged: this lane's row in page 0
     auto kread = [&](int i) {
-        const int ks = i / T2, r = 32 * (i % T2) + ln;
-        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kl + r * Lds<D>::KSTR + (2 * ks + hi) * 16);
+        const int ks = i / T2, t = i % T2;
+        const lds_char* at = PSLOT ? kp + 2 * t * PSLOT : kl + (32 * t + ln) * Lds<D>::KSTR;   // key half t: row 32t
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(at + (2 * ks + hi) * 16);
     };
     bf16x8 kf[NQK];
 #pragma unroll
@@ -468,9 +472,15 @@ __device__ __forceinline__ void finish_partial(const RowState<D>& st, float* oro
 // Page loads: with four waves and 64-key tiles each wave stages exactly one 16-token page of K and one of V. The
 // wave builds one buffer view per page (64-bit base at the page's slab, size clipped at the sequence end, so rows
 // past it and pages the table does not give read zeros) and issues whole 1 KiB direct-to-LDS loads whose per-lane
-// source offsets inside the slab never change. K pages land in an unpadded, XOR-swizzled layout (a page is then a
-// whole number of loads): 16-byte chunk c of row r sits at chunk c ^ swz(r), which spreads any 16 consecutive rows'
-// reads of one chunk over all banks. V keeps the dense kernel's padded layout, whose pages are whole loads already.
+// source offsets inside the slab never change. V keeps the dense kernel's padded layout, whose pages are whole
+// loads already. K takes one of two layouts:
+//   - padded like the dense kernel's (row stride D*2 + 16), each page in a slot rounded up to whole loads (5 KiB at
+//     D = 128: the last load's lanes past row 15 fall outside the page's view and fetch nothing), so the scheduled
+//     QK product reads it at compile-time offsets;
+//   - unpadded and XOR-swizzled (a page is then exactly its loads): 16-byte chunk c of row r sits at chunk
+//     c ^ swz(r), which spreads any 16 consecutive rows' reads of one chunk over all banks, at the cost of address
+//     arithmetic per read. It needs a fifth less load work and LDS per page, which pays on sliding-window chunks,
+//     whose short walks are bound by their loads.
 template <int D>
 struct SwzK {
     static constexpr int ROWB = D * 2;
@@ -484,9 +494,8 @@ template <int D, int ROWSTR, bool SWZ>
 struct PageLoader {
     static constexpr int ROWB = D * 2;
     static constexpr int CPR = ROWB / 16;
-    static constexpr int PAGEB = kPageTokens * ROWSTR;   // LDS bytes of one page
-    static constexpr int LPP = PAGEB / 1024;             // 1 KiB loads per page
-    static_assert(PAGEB % 1024 == 0, "a page must be whole direct loads");
+    static constexpr int LPP = (kPageTokens * ROWSTR + 1023) / 1024;   // 1 KiB loads per page
+    static constexpr int PAGEB = LPP * 1024;   // LDS slot of one page; slots past row 15 lie outside the page's view
     int voff[LPP];
     __device__ __forceinline__ void init(int lane) {
 #pragma unroll
@@ -539,12 +548,16 @@ __device__ __forceinline__ void window_mask(f32x16 (&s)[2], int kv0, int qabs, i
         }
 }
 
-template <int D>
-__global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
-void prefill_paged_kernel(const PagedArgs a) {
+// PADK selects the K layout (padded with the scheduled tile products, or swizzled with the compiler's order). The
+// body is a device function template: with it written in the kernel template itself, the host pass of the compiler
+// left the launch stub of one instantiation undefined.
+template <int D, bool PADK>
+__device__ __forceinline__ void paged_body(const PagedArgs& a) {
     constexpr int NW = kDenseWaves;
     static_assert(NW * kPageTokens == kBN, "one page per wave");
-    __shared__ __attribute__((aligned(1024))) char k0[SwzK<D>::TILE];
+    using KLoader = PageLoader<D, PADK ? Lds<D>::KSTR : SwzK<D>::ROWB, !PADK>;
+    static_assert(PADK || KLoader::PAGEB == kPageTokens * SwzK<D>::ROWB, "swizzled K pages are whole loads");
+    __shared__ __attribute__((aligned(1024))) char k0[NW * KLoader::PAGEB];
     __shared__ __attribute__((aligned(1024))) char v0[Lds<D>::VTILE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -579,8 +592,9 @@ void prefill_paged_kernel(const PagedArgs a) {
     RowState<D> st;
     init_state<D>(st);
 
-    PageLoader<D, SwzK<D>::ROWB, true> lk;
+    KLoader lk;
     PageLoader<D, Lds<D>::VSTR, false> lv;
+    static_assert(NW * decltype(lv)::PAGEB == Lds<D>::VTILE, "V pages fill the dense tile layout");
     lk.init(lane);
     lv.init(lane);
     VtAddr<D> va;
@@ -615,12 +629,14 @@ void prefill_paged_kernel(const PagedArgs a) {
         __syncthreads();
         f32x16 sc[2];
         uint32_t pw[2][8];
-        qk_tile_swz<D>((lds_char*)k0, qf, sc, lane);
+        if constexpr (PADK) qk_tile_sched<D, 2, KLoader::PAGEB>((lds_char*)k0, qf, sc, lane);
+        else qk_tile_swz<D>((lds_char*)k0, qf, sc, lane);
         __syncthreads();   // every wave is done with K(j)
         if (j + 1 < ntiles) lk.load(kn, (lds_char*)k0, w);
         if (a.window > 0 && kv <= q0abs + 31 - a.window) window_mask(sc, kv, qabs, a.window, lane);
         softmax_tile<D>(sc, pw, st, a.c2, kv + kBN - 1 > q0abs, kv, qabs, lane);
-        pv_tile<D>((lds_char*)v0, va, pw, st);
+        if constexpr (PADK) pv_tile_sched<D, 2>((lds_char*)v0, va, pw, st);
+        else pv_tile<D>((lds_char*)v0, va, pw, st);
         __syncthreads();   // and with V(j)
         if (j + 1 < ntiles) lv.load(vn, (lds_char*)v0, w);
         kv = kv_n;
@@ -631,6 +647,12 @@ void prefill_paged_kernel(const PagedArgs a) {
         const size_t prow = ((size_t)blockIdx.y * a.B + b) * a.Hq + h;   // (split, b, h)
         finish_partial<D>(st, a.opart + prow * a.Nq * D, a.lpart + prow * a.Nq, qrow, a.Nq, lane);
     }
+}
+
+template <int D, bool PADK>
+__global__ __launch_bounds__(kDenseWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void prefill_paged_kernel(const PagedArgs a) {
+    paged_body<D, PADK>(a);
 }
 
 // Merge of the key-range splits: each lane merges four head dims of one (b, h, row) with 16-byte loads of the
@@ -885,10 +907,17 @@ hipError_t launch_prefill_paged(const PagedPrefillProblem& p, hipStream_t s) {
     a.opart = static_cast<float*>(p.workspace);
     a.lpart = a.opart + (size_t)p.splits * p.B * p.Hq * p.Nq * p.D;
     const dim3 grid((unsigned)(a.n_ptiles * a.B * a.Hkv * a.NHG), (unsigned)p.splits);
-    if (p.D == 128)
-        hipLaunchKernelGGL((prefill_paged_kernel<128>), grid, dim3(NW * 64), 0, s, a);
-    else
-        hipLaunchKernelGGL((prefill_paged_kernel<64>), grid, dim3(NW * 64), 0, s, a);
+    // padded K with the scheduled products, except for sliding windows, whose short walks are bound by their loads
+    // (windowed chunk: swizzled 0.1155 against padded 0.1199 ms; chunk closing a 32K sequence: padded 1.816 against
+    // swizzled 1.862 ms, bit-identical)
+    const bool padk = p.window <= 0;
+    if (p.D == 128) {
+        if (padk) hipLaunchKernelGGL((prefill_paged_kernel<128, true>), grid, dim3(NW * 64), 0, s, a);
+        else hipLaunchKernelGGL((prefill_paged_kernel<128, false>), grid, dim3(NW * 64), 0, s, a);
+    } else {
+        if (padk) hipLaunchKernelGGL((prefill_paged_kernel<64, true>), grid, dim3(NW * 64), 0, s, a);
+        else hipLaunchKernelGGL((prefill_paged_kernel<64, false>), grid, dim3(NW * 64), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     PagedCombineArgs c;
