@@ -172,7 +172,7 @@ __device__ __forceinline__ float softmax_max(f32x16 (&s)[T2], RowState<D>& st, f
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
-                if (key > qrow) s[t][r] = -INFINITY;
+                s[t][r] = key > qrow ? -INFINITY : s[t][r];
             }
     }
     // one chain of three-input maxima per key half (v_max3_f32: two values per instruction)
@@ -753,18 +753,20 @@ void prefill_sparse_bf16_kernel(const SparseArgs a) {
     RowState<D> st;
     init_state<D>(st);
     if (cnt == 0) return;  // every valid list holds the diagonal; an empty one leaves the rows unwritten
-    // the row's block list goes to LDS once, so the tile loop reads the next tile's block in LDS latency instead
-    // of a global round trip per tile
+    // the row's block list goes to LDS once, as each kept block's first key, so the tile loop finds the next tile's
+    // first key with an LDS read and an add instead of a global round trip per tile
     extern __shared__ int lst[];   // nb entries, sized at launch
-    for (int e = tid; e < cnt; e += NW * 64) lst[e] = list[e];
+    const int blk = a.block;
+    for (int e = tid; e < cnt; e += NW * 64) lst[e] = list[e] * blk;
     __syncthreads();
     // the diagonal block (the list's last) is walked only up to this work-group's last row
     const int diag_tiles = ((part + 1) * 32 * NW + BN - 1) / BN;
-    const int ntiles = (cnt - 1) * sub + (lst[cnt - 1] == i ? diag_tiles : sub);
-    const int blk = a.block;
+    const int ntiles = (cnt - 1) * sub + (lst[cnt - 1] == i * blk ? diag_tiles : sub);
+    // sub is a power of two (block / tile: 2 or 4)
+    const int lsub = __builtin_ctz(sub);
     // a tile's first key comes from LDS, which the compiler takes as per-lane; read out once as wave-uniform, so the
     // direct loads get it as their scalar offset instead of looping over lanes for it
-    auto kv_of = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[t / sub] * blk + (t % sub) * BN); };
+    auto kv_of = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[t >> lsub] + (t & (sub - 1)) * BN); };
     attend_sb<D, NW, decltype(kv_of), T2>((lds_char*)k0, (lds_char*)v0, krs, vrs, ntiles, kv_of, qf, st, a.c2, q0,
                                           w, lane);
     finish_rows<D>(st, a.o + qoff, a.lse ? a.lse + ((size_t)b * a.Hq + h) * a.N : nullptr, qrow, a.N, lane);
