@@ -303,6 +303,33 @@ def test_sparse_full_size_sampled(lib, name, mode):
     assert eo <= BF16_TOL and el <= LSE_TOL
 
 
+def test_sparse_largest_block_count(lib):
+    """The sparse kernel at the library's largest block count: 4096 key blocks of 64 rows (N = 262144), so each
+    row's kept list takes 16 KiB of LDS beside the tiles. Sampled rows against the oracle over the oracle's lists,
+    the last row of the sequence included."""
+    N, blk = 262144, 64
+    inp = W.planted_inputs(49, 1, 2, 1, N, 64, blk)
+    q, k, v = inp.as_f64()
+    say("[sparse] largest nb=4096: oracle mask")
+    ref = M.build_mask(q, k, inp.scale, blk, 30, 1.0)
+    del q
+    o, lse = run_sparse(lib, inp, ref.kv_count, ref.kv_index)
+    rows = W.sample_rows(49, N, 2, 48, block=blk, planted=inp.planted)
+    og, lg = take_rows(o, rows), take_rows(lse.unsqueeze(-1), rows)[..., 0]
+    del o, lse
+    Oref = np.zeros_like(og)
+    Lref = np.zeros_like(lg)
+    for h in range(2):
+        qh = np.zeros((1, 1, N, 64))
+        qh[:, 0, rows[h]] = W.f64_from_bf16_bits(inp.q[:, h, rows[h]])
+        o_h, l_h = A.masked_attention(qh, k, v, inp.scale, ref.mask[:, h:h + 1], blk, rows=rows[h])
+        Oref[:, h], Lref[:, h] = o_h[:, 0], l_h[:, 0]
+    eo, el = max_err(og, Oref), max_err(lg, Lref)
+    say(f"[sparse] largest nb=4096: max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= BF16_TOL and el <= LSE_TOL
+    torch.cuda.empty_cache()
+
+
 def test_sparse_deterministic(lib):
     inp = W.planted_inputs(45, 1, 8, 2, 64 * 16, 128, 64)
     q, k, v = inp.as_f64()
