@@ -89,7 +89,7 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the 32K/128K dense and 128K sparse lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--long-reps", type=int, default=20)
-    ap.add_argument("--cpu-rows", type=int, default=1024,
+    ap.add_argument("--cpu-rows", type=int, default=3200,
                     help="query rows per head the CPU oracle computes for cpu_baseline")
     ap.add_argument("--only", choices=["dense", "dense32k", "sparse", "sparse128k", "decode", "decode8", "paged",
                                        "copy"],
